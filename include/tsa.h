@@ -1,0 +1,156 @@
+/*
+ * tsa.h - C ABI of the Token Sparse Attention prefill library (libtsa.so).
+ *
+ * Method: "Token Sparse Attention: Efficient Long-Context Inference with
+ * Interleaved Token Selection" (Jo, Kang, Song, Kim, 2026).  The method
+ * detail is in the gist.science summary, section 2 "Methodology":
+ *   - "Core architecture", stage 1 (compression): per attention head a set
+ *     S_h of token indices is chosen from importance scores, and Q, K, V are
+ *     gathered into dense, contiguous tensors of reduced length L' << L;
+ *     selection is independent per head.
+ *   - "Core architecture", stage 2 (decompression): the L' x d output is
+ *     scattered back into a zero-initialised L x d tensor at the head's
+ *     indices; unselected positions are zero.
+ *   - "Dynamic Token Coverage": importance comes from a light proxy attention
+ *     map of recent queries against all keys, summed column-wise; tokens are
+ *     sorted by ascending importance and the tail is pruned while the pruned
+ *     mass stays within a coverage threshold tau, which fixes one global
+ *     budget; then every head takes its own top-k.
+ *
+ * Conventions shared by every entry point:
+ *   - Memory: every tensor pointer is DEVICE memory allocated and owned by the
+ *     caller.  The library never allocates, frees or synchronises the host;
+ *     all work is enqueued on `stream` (a hipStream_t; NULL = null stream)
+ *     and the call returns once it is enqueued.
+ *   - Layout: row-major contiguous.  Q is [B,Hq,L,d], K and V are
+ *     [B,Hkv,L,d], in `dtype` (TSA_F32 = float, TSA_BF16 = bfloat16).  Tensor
+ *     pointers must be 16-byte aligned.  Offsets are 64-bit.
+ *   - GQA: query head h uses KV head h / (Hq/Hkv).
+ *   - Budget: the per-sequence budget K_b stays on the device ([B] int32).
+ *     Compact per-head buffers have capacity L rows; kernels read K_b, so no
+ *     host read-back happens anywhere and the sequence is graph-capturable.
+ *   - Validation is synchronous and happens before anything is enqueued.
+ *     TSA_ERR_INVALID_ARG: a null problem or tensor pointer, a misaligned
+ *     tensor pointer, any dimension < 1, Hq % Hkv != 0, w > L, Hq > 4096,
+ *     L > 2^28, tau outside [0, 1) or NaN, a bad kv_group.
+ *     TSA_ERR_UNSUPPORTED: d not in {64, 128} or an unknown dtype.
+ *     TSA_ERR_WORKSPACE: ws_bytes below what the *_workspace_bytes query
+ *     returns, or a null / misaligned (256 B) workspace.
+ *     TSA_ERR_HIP: a launch failed; tsa_last_error() holds the detail.
+ *   - Threading: no global mutable state except the thread-local error text;
+ *     concurrent calls on different streams with different buffers are safe.
+ */
+#ifndef TSA_H_
+#define TSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tsa_status {
+  TSA_OK = 0,
+  TSA_ERR_INVALID_ARG = 1,
+  TSA_ERR_UNSUPPORTED = 2,
+  TSA_ERR_WORKSPACE = 3,
+  TSA_ERR_HIP = 4
+} tsa_status;
+
+typedef enum tsa_dtype { TSA_F32 = 0, TSA_BF16 = 1 } tsa_dtype;
+
+/* Problem shape.  w: number of proxy (most recent) queries; tau: coverage
+ * threshold in [0, 1).  dtype: a tsa_dtype value. */
+typedef struct tsa_problem {
+  int32_t B, Hq, Hkv, L, d, w;
+  float tau;
+  int32_t dtype;
+} tsa_problem;
+
+/* Human-readable name of a status code (static storage). */
+const char* tsa_status_string(tsa_status st);
+
+/* Detail text of the last failing call on this thread ("" if none). */
+const char* tsa_last_error(void);
+
+/* Library version string, e.g. "tsa 0.1 gfx950". */
+const char* tsa_version(void);
+
+/* Scratch bytes needed by tsa_score, tsa_budget and tsa_select (one buffer
+ * serves all three; it need not be cleared).  0 on an invalid problem. */
+size_t tsa_workspace_bytes(const tsa_problem* prob);
+
+/* Scratch bytes needed by tsa_forward: the step scratch plus the
+ * intermediate scores, rank map and the four compact per-head tensors. */
+size_t tsa_forward_workspace_bytes(const tsa_problem* prob);
+
+/* Proxy scoring ("Dynamic Token Coverage", scoring).  For every query head h
+ * and proxy row r in [L-w, L): logits x_rj = <Q[b,h,r], K[b,g(h),j]>/sqrt(d)
+ * over the causally visible keys j <= r, one softmax per row, and
+ *   s[b,h,j] = (1/w) * sum_r p_rj        (each head's row sums to 1).
+ * q: [B,Hq,L,d] (only the last w rows are read); k: [B,Hkv,L,d];
+ * s: [B,Hq,L] float32 output.  Deterministic (fixed reduction order). */
+tsa_status tsa_score(const tsa_problem* prob, const void* q, const void* k, float* s,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Global budget ("Dynamic Token Coverage", budget allocation).  Per batch
+ * element: sigma_j = sum_h floor(clip(s[b,h,j],0,1) * 2^50) (exact integers),
+ * C(p) = sum of the p smallest sigma_j, P = max{p in [0,L-1] :
+ * C(p) <= Hq*tau*2^50} (P = 0 when tau = 0), budget[b] = L - P.  This is the
+ * head-mean pruned mass compared with tau, counted exactly in units of
+ * 2^-50.  Scores whose per-head sums exceed 1 + 2^-10 (not produced by
+ * tsa_score) give an unspecified but in-range budget.
+ * s: [B,Hq,L] float32; budget: [B] int32 output. */
+tsa_status tsa_budget(const tsa_problem* prob, const float* s, int32_t* budget,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Per-head top-K ("Dynamic Token Coverage", per-head selection), K = budget[b].
+ * Tokens are ranked by (s descending, index ascending); NaN and negative
+ * scores rank as 0.  idx[b,h,0..K) receives the chosen indices in ascending
+ * order and idx[b,h,K..L) = -1; rank[b,h,j] = position of j in that list,
+ * or -1.  s: [B,Hq,L] float32; budget: [B] int32 (device, 1..L);
+ * idx, rank: [B,Hq,L] int32 outputs. */
+tsa_status tsa_select(const tsa_problem* prob, const float* s, const int32_t* budget,
+                      int32_t* idx, int32_t* rank, void* ws, size_t ws_bytes, void* stream);
+
+/* Compression ("Core architecture", stage 1).  For i < K_b:
+ *   qc[b,h,i] = Q[b,h,idx_i], kc[b,h,i] = K[b,g(h),idx_i], vc[b,h,i] = V[b,g(h),idx_i].
+ * Rows i >= K_b of qc/kc/vc are not written.  q: [B,Hq,L,d]; k, v:
+ * [B,Hkv,L,d]; idx: [B,Hq,L] int32 (first K_b entries in [0,L));
+ * qc, kc, vc: [B,Hq,L,d] outputs.  Bit-exact copies. */
+tsa_status tsa_gather(const tsa_problem* prob, const void* q, const void* k, const void* v,
+                      const int32_t* idx, const int32_t* budget, void* qc, void* kc, void* vc,
+                      void* stream);
+
+/* Causal attention on dense tensors (the compressed tensors, or the
+ * uncompressed ones for the dense baseline).  For i < n:
+ *   o[b,h,i] = sum_{j<=i} softmax_j(<q[b,h,i], k[b,h/kv_group,j]>/sqrt(d)) v[b,h/kv_group,j]
+ * with n = budget[b] (device) or n = L when budget is NULL.  kv_group = 1 for
+ * the compact per-head K/V (k, v: [B,Hq,L,d]); kv_group = Hq/Hkv for the
+ * dense GQA layout (k, v: [B,Hkv,L,d]).  Rows i >= n of o are not written.
+ * bf16: bf16 MFMA products, fp32 accumulation and softmax, output rounded
+ * to nearest even; f32: fp32 throughout. */
+tsa_status tsa_attention(const tsa_problem* prob, const void* q, const void* k, const void* v,
+                         const int32_t* budget, int32_t kv_group, void* o, void* stream);
+
+/* Decompression ("Core architecture", stage 2).  For every j < L:
+ *   o[b,h,j] = rank[b,h,j] >= 0 ? oc[b,h,rank[b,h,j]] : +0.0
+ * Each output row is written exactly once.  oc: [B,Hq,L,d]; rank: [B,Hq,L]
+ * int32 (values in [-1, L)); o: [B,Hq,L,d] output. */
+tsa_status tsa_scatter(const tsa_problem* prob, const void* oc, const int32_t* rank, void* o,
+                       void* stream);
+
+/* The whole op: score -> budget -> select -> gather -> attention -> scatter.
+ * o: [B,Hq,L,d] output (unselected rows exactly zero); budget: [B] int32
+ * output; idx: [B,Hq,L] int32 output (as tsa_select).  ws must hold
+ * tsa_forward_workspace_bytes(prob) bytes. */
+tsa_status tsa_forward(const tsa_problem* prob, const void* q, const void* k, const void* v,
+                       void* o, int32_t* budget, int32_t* idx, void* ws, size_t ws_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSA_H_ */

@@ -1,0 +1,161 @@
+"""The C ABI on the host: symbols, workspace sizing, validation (no GPU needed).
+
+Only invalid arguments are passed with placeholder pointers: validation
+rejects them before anything is enqueued, so no kernel ever runs here.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from token_sparse_attention_proxy_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tsa.h")
+FAKE = 1 << 20          # aligned placeholder pointer value; never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from token_sparse_attention_proxy_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tsa_[a-z_]+)\s*\(", text)))
+
+
+def prob(**kw):
+    base = dict(B=1, Hq=8, Hkv=2, L=1000, d=128, w=64, tau=0.05, dtype=_lib.TSA_BF16)
+    base.update(kw)
+    return _lib.TsaProblem(**base)
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = declared_symbols()
+    assert set(syms) == set(_lib.EXPORTS), syms
+    for name in syms:
+        assert hasattr(lib, name), name
+
+
+def test_nm_lists_exports():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    for name in declared_symbols():
+        assert re.search(rf"\bT {name}$", out, re.M), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.tsa_version().decode().startswith("tsa ")
+    names = [lib.tsa_status_string(i).decode() for i in range(5)]
+    assert names == ["TSA_OK", "TSA_ERR_INVALID_ARG", "TSA_ERR_UNSUPPORTED", "TSA_ERR_WORKSPACE",
+                     "TSA_ERR_HIP"]
+
+
+def test_workspace_sizes(lib):
+    p = prob()
+    step = lib.tsa_workspace_bytes(ctypes.byref(p))
+    fwd = lib.tsa_forward_workspace_bytes(ctypes.byref(p))
+    assert step > 0 and step % 256 == 0
+    # forward scratch holds at least scores, rank and four compact tensors
+    assert fwd >= step + 4 * 8 * 1000 * 2 + 4 * 8 * 1000 * 128 * 2
+    assert lib.tsa_workspace_bytes(ctypes.byref(prob(Hkv=3))) == 0
+    assert lib.tsa_workspace_bytes(None) == 0
+
+
+def test_workspace_scales_with_headline_shape(lib):
+    p = prob(Hq=32, Hkv=8, L=131072, w=64)
+    fwd = lib.tsa_forward_workspace_bytes(ctypes.byref(p))
+    tens = 32 * 131072 * 128 * 2
+    assert 4 * tens < fwd < 4 * tens + 64 * 2 ** 20
+
+
+BAD_PROBLEMS = [
+    (dict(B=0), _lib.TSA_ERR_INVALID_ARG),
+    (dict(Hq=0), _lib.TSA_ERR_INVALID_ARG),
+    (dict(Hkv=3), _lib.TSA_ERR_INVALID_ARG),
+    (dict(L=0), _lib.TSA_ERR_INVALID_ARG),
+    (dict(w=0), _lib.TSA_ERR_INVALID_ARG),
+    (dict(w=1001), _lib.TSA_ERR_INVALID_ARG),
+    (dict(tau=-0.01), _lib.TSA_ERR_INVALID_ARG),
+    (dict(tau=1.0), _lib.TSA_ERR_INVALID_ARG),
+    (dict(tau=float("nan")), _lib.TSA_ERR_INVALID_ARG),
+    (dict(Hq=8192, Hkv=8192), _lib.TSA_ERR_INVALID_ARG),
+    (dict(d=96), _lib.TSA_ERR_UNSUPPORTED),
+    (dict(d=256), _lib.TSA_ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.TSA_ERR_UNSUPPORTED),
+]
+
+
+def _call_all(lib, p, ptr=FAKE, ws_bytes=1 << 40, kv_group=1):
+    P = ctypes.byref(p)
+    return {
+        "score": lib.tsa_score(P, ptr, ptr, ptr, ptr, ws_bytes, None),
+        "budget": lib.tsa_budget(P, ptr, ptr, ptr, ws_bytes, None),
+        "select": lib.tsa_select(P, ptr, ptr, ptr, ptr, ptr, ws_bytes, None),
+        "gather": lib.tsa_gather(P, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, None),
+        "attention": lib.tsa_attention(P, ptr, ptr, ptr, ptr, kv_group, ptr, None),
+        "scatter": lib.tsa_scatter(P, ptr, ptr, ptr, None),
+        "forward": lib.tsa_forward(P, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ws_bytes, None),
+    }
+
+
+@pytest.mark.parametrize("kw,status", BAD_PROBLEMS, ids=[str(k) for k, _ in BAD_PROBLEMS])
+def test_bad_problem_rejected_everywhere(lib, kw, status):
+    res = _call_all(lib, prob(**kw))
+    assert set(res.values()) == {status}, res
+    assert lib.tsa_last_error().decode() != ""
+
+
+def test_null_problem(lib):
+    assert lib.tsa_score(None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == _lib.TSA_ERR_INVALID_ARG
+    assert "NULL" in lib.tsa_last_error().decode()
+
+
+def test_null_and_misaligned_pointers(lib):
+    p = prob()
+    res = _call_all(lib, p, ptr=None)
+    assert set(res.values()) == {_lib.TSA_ERR_INVALID_ARG}, res
+    res = _call_all(lib, p, ptr=FAKE + 8)
+    assert set(res.values()) == {_lib.TSA_ERR_INVALID_ARG}, res
+    assert "aligned" in lib.tsa_last_error().decode()
+
+
+def test_workspace_too_small(lib):
+    p = prob()
+    P = ctypes.byref(p)
+    need = lib.tsa_workspace_bytes(P)
+    for st in [lib.tsa_score(P, FAKE, FAKE, FAKE, FAKE, need - 1, None),
+               lib.tsa_budget(P, FAKE, FAKE, FAKE, need - 1, None),
+               lib.tsa_select(P, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None)]:
+        assert st == _lib.TSA_ERR_WORKSPACE
+    fneed = lib.tsa_forward_workspace_bytes(P)
+    assert lib.tsa_forward(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, fneed - 1, None) == \
+        _lib.TSA_ERR_WORKSPACE
+    # misaligned workspace
+    assert lib.tsa_score(P, FAKE, FAKE, FAKE, FAKE + 16, need, None) == _lib.TSA_ERR_WORKSPACE
+
+
+def test_bad_kv_group(lib):
+    p = prob()
+    P = ctypes.byref(p)
+    for g in (0, -1, 3, 16):
+        assert lib.tsa_attention(P, FAKE, FAKE, FAKE, None, g, FAKE, None) == _lib.TSA_ERR_INVALID_ARG
+
+
+def test_injected_launch_failure_propagates(lib, monkeypatch):
+    """A host-forced launch failure surfaces as TSA_ERR_HIP and as TsaError in Python."""
+    monkeypatch.setenv("TSA_FAULT_INJECT", "launch")
+    p = prob()
+    res = _call_all(lib, p)
+    assert set(res.values()) == {_lib.TSA_ERR_HIP}, res
+    assert "injected" in lib.tsa_last_error().decode()
+    with pytest.raises(_lib.TsaError) as ei:
+        _lib.check(res["forward"], "tsa_forward")
+    assert ei.value.name == "TSA_ERR_HIP"

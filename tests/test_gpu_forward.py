@@ -1,0 +1,120 @@
+"""tsa_forward end to end against the fp64 oracle (GPU).
+
+Small workloads are compared in full.  The five named workloads run at their
+full sizes in the launch configuration the bench times; there the oracle
+computes every score, budget and index set, and output rows are sampled.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import tsa_oracle as O
+from tests.parity import assert_scores_close, compare_forward, say, to_dev, to_np
+from token_sparse_attention_proxy_amd import inputs
+from token_sparse_attention_proxy_amd import tsa as T
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    inputs.small_workload("bf16", B=1, Hq=8, Hkv=2, L=1000, d=128, w=64, tau=0.05, seed_base=9300),
+    inputs.small_workload("bf16", B=2, Hq=6, Hkv=2, L=700, d=128, w=32, tau=0.2, plant_frac=0.02,
+                          plant_amp=5.0, seed_base=9310),
+    inputs.small_workload("bf16", B=1, Hq=4, Hkv=4, L=513, d=64, w=16, tau=0.1, seed_base=9320),
+    inputs.small_workload("bf16", B=1, Hq=4, Hkv=1, L=2048, d=128, w=64, tau=0.3, zipf_s=1.1,
+                          plant="none", seed_base=9330),
+    inputs.small_workload("f32", B=1, Hq=4, Hkv=2, L=600, d=64, w=16, tau=0.05, seed_base=9340),
+    inputs.small_workload("bf16", B=1, Hq=2, Hkv=2, L=3, d=128, w=2, tau=0.5, seed_base=9350),
+]
+
+
+def run_forward(wl, tau):
+    q, k, v = inputs.make_qkv(wl)
+    prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, float(tau), wl.dtype)
+    qd, kd, vd = to_dev(q, wl.dtype), to_dev(k, wl.dtype), to_dev(v, wl.dtype)
+    o, budget, idx = T.tsa_forward(prob, qd, kd, vd)
+    torch.cuda.synchronize()
+    return q, k, v, to_np(o), to_np(budget), to_np(idx), o
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_forward_small(wl):
+    tau = wl.taus[0]
+    say(f"case forward {wl.name} tau={tau}")
+    q, k, v, o, budget, idx, o_dev = run_forward(wl, tau)
+    ref = O.forward(q, k, v, wl.w, tau)
+    say(f"  budget gpu {budget} oracle {ref['budget']} (K/L {budget / wl.L})")
+    compare_forward(ref, o, budget, idx, q, k, v, tau, wl.dtype)
+    sel = np.zeros(idx.shape, bool)
+    for b in range(wl.B):
+        for h in range(wl.Hq):
+            sel[b, h, idx[b, h, :budget[b]]] = True
+    bits = o_dev.view(torch.int16 if wl.dtype == "bf16" else torch.int32)
+    assert torch.all(bits[torch.from_numpy(~sel).cuda()] == 0)
+
+
+def test_forward_deterministic():
+    wl = SMALL[0]
+    say("case forward determinism")
+    q, k, v = inputs.make_qkv(wl)
+    prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, 0.05, wl.dtype)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    a = T.tsa_forward(prob, qd, kd, vd)
+    b = T.tsa_forward(prob, qd, kd, vd)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+def test_steps_compose_to_forward():
+    """The seven entry points called one by one give the fused call's result bit for bit."""
+    wl = SMALL[1]
+    say("case steps == forward")
+    q, k, v = inputs.make_qkv(wl)
+    prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, 0.2, wl.dtype)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    o, budget, idx = T.tsa_forward(prob, qd, kd, vd)
+    s = T.tsa_score(prob, qd, kd)
+    bud = T.tsa_budget(prob, s)
+    idx2, rank = T.tsa_select(prob, s, bud)
+    qc, kc, vc = T.tsa_gather(prob, qd, kd, vd, idx2, bud)
+    oc = T.tsa_attention(prob, qc, kc, vc, bud, 1)
+    o2 = T.tsa_scatter(prob, oc, rank)
+    assert torch.equal(budget, bud) and torch.equal(idx, idx2)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+
+
+# ---------------------------------------------------------------- full sizes
+FULL = ["tiny_mha_f32_L1k", "llama8b_bf16_L8k", "llama8b_bf16_L32k_zipf", "llama8b_bf16_L128k",
+        "gqa7_bf16_B2_L64k"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_size(name):
+    wl = inputs.WORKLOADS[name]
+    say(f"case forward full {name}: generating inputs")
+    q, k, v = inputs.make_qkv(wl)
+    qd, kd, vd = to_dev(q, wl.dtype), to_dev(k, wl.dtype), to_dev(v, wl.dtype)
+    say("  oracle scores")
+    s_ref = O.proxy_scores(q, k, wl.w)
+    for tau in wl.taus:
+        prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, float(tau), wl.dtype)
+        s_gpu = to_np(T.tsa_score(prob, qd, kd))
+        assert_scores_close(s_gpu, s_ref, f" {name}")
+        o, budget, idx = T.tsa_forward(prob, qd, kd, vd)
+        torch.cuda.synchronize()
+        budget_np, idx_np = to_np(budget), to_np(idx)
+        say(f"  tau={tau}: budget {budget_np} K/L {budget_np / wl.L}")
+        b_ref = O.coverage_budget(s_ref, tau)
+        idx_ref, _ = O.select_heads(s_ref, b_ref)
+        ref = {"s": s_ref, "budget": b_ref, "idx": idx_ref}
+        sample = 0 if wl.L <= 1024 else 6
+        if sample == 0:
+            qc, kc, vc = O.gather(q, k, v, idx_ref, b_ref)
+            ref["o"] = O.scatter(O.attention_heads(qc, kc, vc, b_ref), idx_ref, b_ref)
+        o_np = to_np(o)
+        compare_forward(ref, o_np, budget_np, idx_np, q, k, v, tau, wl.dtype, sample_rows=sample,
+                        seed=int(tau * 1000))
+        del o, budget, idx
+    del qd, kd, vd
+    torch.cuda.empty_cache()

@@ -1,0 +1,230 @@
+"""Each C-ABI entry point against the fp64 oracle on the same seeded inputs (GPU).
+
+Inputs come from token_sparse_attention_proxy_amd.inputs only; no oracle
+input is ever taken from the HIP path.  Sizes span several tiles plus a
+ragged tail and stay small enough for the oracle to finish in seconds.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import tsa_oracle as O
+from tests.parity import (assert_outputs_close, assert_scores_close, say, to_dev, to_np)
+from token_sparse_attention_proxy_amd import inputs
+from token_sparse_attention_proxy_amd import tsa as T
+
+pytestmark = pytest.mark.gpu
+
+
+def _problem(wl, tau=None):
+    return T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, float(wl.taus[0] if tau is None else tau),
+                     wl.dtype)
+
+
+SCORE_CASES = [
+    inputs.small_workload("bf16", B=1, Hq=8, Hkv=2, L=1000, d=128, w=64, seed_base=9100),
+    inputs.small_workload("bf16", B=2, Hq=4, Hkv=4, L=513, d=64, w=33, seed_base=9110),
+    inputs.small_workload("bf16", B=1, Hq=6, Hkv=2, L=300, d=128, w=300, seed_base=9120),
+    inputs.small_workload("bf16", B=1, Hq=2, Hkv=1, L=5, d=128, w=1, seed_base=9130),
+    inputs.small_workload("f32", B=1, Hq=4, Hkv=4, L=700, d=64, w=16, seed_base=9140),
+    inputs.small_workload("f32", B=1, Hq=4, Hkv=2, L=257, d=128, w=20, seed_base=9150),
+    inputs.small_workload("bf16", B=1, Hq=4, Hkv=1, L=2048, d=128, w=128, zipf_s=1.1,
+                          plant="none", seed_base=9160),
+]
+
+
+@pytest.mark.parametrize("wl", SCORE_CASES, ids=[w.name for w in SCORE_CASES])
+def test_score_matches_oracle(wl):
+    say(f"case score {wl.name}")
+    q, k, _ = inputs.make_qkv(wl)
+    s = to_np(T.tsa_score(_problem(wl), to_dev(q, wl.dtype), to_dev(k, wl.dtype)))
+    torch.cuda.synchronize()
+    ref = O.proxy_scores(q, k, wl.w)
+    assert_scores_close(s, ref, f" {wl.name}")
+    assert np.allclose(s.sum(-1), 1.0, atol=1e-5)
+
+
+def test_score_deterministic():
+    wl = SCORE_CASES[0]
+    say("case score determinism")
+    q, k, _ = inputs.make_qkv(wl)
+    qd, kd = to_dev(q, wl.dtype), to_dev(k, wl.dtype)
+    a = T.tsa_score(_problem(wl), qd, kd)
+    b = T.tsa_score(_problem(wl), qd, kd)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+BUDGET_CASES = [
+    # (B, Hq, L, seed, ties, zero_frac, alpha)
+    (1, 8, 1000, 1, False, 0.0, 1.0),
+    (2, 32, 8192, 2, False, 0.0, 0.3),
+    (2, 4, 777, 3, True, 0.0, 1.0),
+    (1, 3, 5000, 4, False, 0.5, 0.2),
+    (1, 1, 1, 5, False, 0.0, 1.0),
+    (3, 2, 64, 6, True, 0.3, 1.0),
+    (1, 28, 4096, 7, False, 0.0, 5.0),
+]
+
+
+@pytest.mark.parametrize("case", BUDGET_CASES, ids=[str(c) for c in BUDGET_CASES])
+def test_budget_matches_oracle(case):
+    B, Hq, L, seed, ties, zf, alpha = case
+    say(f"case budget {case}")
+    s = inputs.make_scores(B, Hq, L, seed=seed, ties=ties, zero_frac=zf, alpha=alpha)
+    sd = to_dev(s, "f32")
+    for tau in (0.0, 1e-4, 0.01, 0.05, 0.1, 0.3, 0.5, 0.9, 0.999):
+        prob = T.Problem(B, Hq, Hq, L, 128, 1, tau, "bf16")
+        got = to_np(T.tsa_budget(prob, sd))
+        want = O.coverage_budget(s.astype(np.float64), tau)
+        assert np.array_equal(got, want), (tau, got, want)
+
+
+def test_budget_exact_boundary():
+    """tau equal to a pruned-mass value: the token at the boundary is pruned (<=)."""
+    say("case budget boundary")
+    L, Hq = 16, 2
+    s = np.zeros((1, Hq, L), np.float32)
+    s[0, :, :] = 1.0 / 16.0           # every token has head-mean mass 1/16
+    sd = to_dev(s, "f32")
+    for p in range(1, 8):
+        tau = p / 16.0
+        got = int(to_np(T.tsa_budget(T.Problem(1, Hq, Hq, L, 64, 1, tau, "f32"), sd))[0])
+        assert got == L - p == int(O.coverage_budget(s, tau)[0])
+
+
+SELECT_CASES = [
+    (1, 8, 1000, 11, False),
+    (2, 4, 4096, 12, True),
+    (1, 3, 1, 13, False),
+    (1, 5, 3000, 14, True),
+    (2, 6, 1025, 15, False),
+]
+
+
+@pytest.mark.parametrize("case", SELECT_CASES, ids=[str(c) for c in SELECT_CASES])
+def test_select_matches_oracle(case):
+    B, H, L, seed, ties = case
+    say(f"case select {case}")
+    s = inputs.make_scores(B, H, L, seed=seed, ties=ties, zero_frac=0.1 if ties else 0.0)
+    rng = np.random.default_rng(seed)
+    sd = to_dev(s, "f32")
+    for K in sorted({1, L, int(rng.integers(1, L + 1)), max(1, L // 2), max(1, L - 1)}):
+        budget = np.array([K] * B, np.int32)
+        if B > 1:
+            budget[-1] = max(1, K // 3)
+        bd = torch.from_numpy(budget).cuda()
+        idx, rank = T.tsa_select(T.Problem(B, H, H, L, 128, 1, 0.05, "bf16"), sd, bd)
+        ridx, rrank = O.select_heads(s.astype(np.float64), budget)
+        assert np.array_equal(to_np(idx), ridx), K
+        assert np.array_equal(to_np(rank), rrank), K
+
+
+def test_select_special_values():
+    """NaN, negative and -0.0 scores rank as 0; +inf ranks first."""
+    say("case select special values")
+    L = 300
+    s = np.abs(np.random.default_rng(3).standard_normal((1, 1, L))).astype(np.float32)
+    s[0, 0, 5] = np.nan
+    s[0, 0, 6] = -1.0
+    s[0, 0, 7] = -0.0
+    s[0, 0, 8] = np.inf
+    s[0, 0, 9] = 0.0
+    bd = torch.tensor([L - 2], dtype=torch.int32, device="cuda")
+    idx, rank = T.tsa_select(T.Problem(1, 1, 1, L, 128, 1, 0.05, "bf16"), to_dev(s, "f32"), bd)
+    clean = np.where(np.isnan(s) | (s <= 0), 0.0, s).astype(np.float64)
+    ridx, rrank = O.select_heads(clean, np.array([L - 2]))
+    assert np.array_equal(to_np(idx), ridx)
+    assert np.array_equal(to_np(rank), rrank)
+    assert 8 in set(to_np(idx)[0, 0, :L - 2])
+
+
+GATHER_CASES = [
+    ("bf16", 1, 8, 2, 1000, 128, 700),
+    ("bf16", 2, 4, 4, 513, 64, 1),
+    ("f32", 1, 4, 2, 300, 64, 300),
+    ("f32", 1, 2, 1, 129, 128, 77),
+]
+
+
+@pytest.mark.parametrize("case", GATHER_CASES, ids=[str(c) for c in GATHER_CASES])
+def test_gather_scatter_bit_exact(case):
+    dt, B, Hq, Hkv, L, d, K = case
+    say(f"case gather/scatter {case}")
+    q = inputs.make_dense((B, Hq, L, d), 21, dt)
+    k = inputs.make_dense((B, Hkv, L, d), 22, dt)
+    v = inputs.make_dense((B, Hkv, L, d), 23, dt)
+    budget = np.array([K] + [max(1, K // 2)] * (B - 1), np.int32)
+    idx, rank = inputs.make_indices(B, Hq, L, budget, seed=24)
+    prob = T.Problem(B, Hq, Hkv, L, d, 1, 0.05, dt)
+    bd = torch.from_numpy(budget).cuda()
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    # canary: rows >= K must stay untouched
+    fill = torch.full((B, Hq, L, d), 7.0, dtype=qd.dtype, device="cuda")
+    qc, kc, vc = T.tsa_gather(prob, qd, kd, vd, torch.from_numpy(idx).cuda(), bd,
+                              fill.clone(), fill.clone(), fill.clone())
+    rq, rk, rv = O.gather(q, k, v, idx, budget)
+    for b in range(B):
+        n = int(budget[b])
+        for got, want in ((qc, rq), (kc, rk), (vc, rv)):
+            g = to_np(got)[b, :, :n]
+            assert np.array_equal(g, want[b, :, :n])
+            assert np.all(to_np(got)[b, :, n:] == 7.0)
+    # scatter of a random compact output
+    oc = inputs.make_dense((B, Hq, L, d), 25, dt)
+    o = T.tsa_scatter(prob, to_dev(oc, dt), torch.from_numpy(rank).cuda())
+    want = O.scatter(oc, idx, budget)
+    assert np.array_equal(to_np(o), want)
+    bits = o.view(torch.int16 if dt == "bf16" else torch.int32)
+    unsel = torch.from_numpy(rank < 0).cuda()
+    assert torch.all(bits[unsel] == 0), "unselected rows must be +0.0 bit patterns"
+
+
+ATTN_CASES = [
+    # dtype, B, Hq, Hkv(k/v heads), L, d, budgets (None = dense), kv_group
+    ("bf16", 1, 4, 4, 1000, 128, [1000], 1),
+    ("bf16", 2, 4, 4, 777, 128, [777, 300], 1),
+    ("bf16", 1, 8, 2, 1000, 128, None, 4),
+    ("bf16", 1, 3, 3, 129, 128, [1], 1),
+    ("bf16", 1, 2, 2, 64, 128, [64], 1),
+    ("bf16", 2, 4, 2, 600, 64, None, 2),
+    ("bf16", 1, 2, 2, 1500, 64, [1337], 1),
+    ("f32", 1, 4, 4, 1000, 64, [900], 1),
+    ("f32", 1, 4, 2, 300, 128, None, 2),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[str(c) for c in ATTN_CASES])
+def test_attention_matches_oracle(case):
+    dt, B, Hq, Hk, L, d, budgets, G = case
+    say(f"case attention {case}")
+    q = inputs.make_dense((B, Hq, L, d), 31, dt)
+    k = inputs.make_dense((B, Hk, L, d), 32, dt, scale=1.5)
+    v = inputs.make_dense((B, Hk, L, d), 33, dt)
+    prob = T.Problem(B, Hq, Hq // G, L, d, 1, 0.05, dt)
+    bd = None if budgets is None else torch.tensor(budgets, dtype=torch.int32, device="cuda")
+    o_init = torch.full((B, Hq, L, d), float("nan"), dtype=torch.bfloat16 if dt == "bf16" else torch.float32,
+                        device="cuda")
+    o = to_np(T.tsa_attention(prob, to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), bd, G, o_init))
+    for b in range(B):
+        n = L if budgets is None else budgets[b]
+        for h in range(Hq):
+            g = h // G
+            ref = O.causal_attention(q[b, h, :n], k[b, g, :n], v[b, g, :n])
+            assert_outputs_close(o[b, h, :n], ref, dt, what=f" b={b} h={h}", quiet=True)
+            assert np.all(np.isnan(o[b, h, n:])), "rows beyond the budget must not be written"
+    say("  ok")
+
+
+def test_attention_deterministic_and_tau0_equals_dense():
+    """TSA at tau = 0 keeps every token, so it is the dense kernel bit for bit."""
+    wl = inputs.small_workload("bf16", B=1, Hq=8, Hkv=2, L=1000, d=128, w=64, seed_base=9200)
+    say("case tau=0 vs dense")
+    q, k, v = inputs.make_qkv(wl)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    prob = T.Problem(1, 8, 2, 1000, 128, 64, 0.0, "bf16")
+    o, budget, idx = T.tsa_forward(prob, qd, kd, vd)
+    dense = T.tsa_attention(prob, qd, kd, vd, None, 4)
+    dense2 = T.tsa_attention(prob, qd, kd, vd, None, 4)
+    assert int(budget[0]) == 1000
+    assert torch.equal(dense.view(torch.int16), dense2.view(torch.int16))
+    assert torch.equal(o.view(torch.int16), dense.view(torch.int16))

@@ -1,0 +1,79 @@
+"""ctypes view of libtsa.so (declared in include/tsa.h).
+
+Argument marshalling only: every step of the op runs in the library's HIP
+kernels.  Loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtsa.so")
+
+TSA_OK, TSA_ERR_INVALID_ARG, TSA_ERR_UNSUPPORTED, TSA_ERR_WORKSPACE, TSA_ERR_HIP = range(5)
+TSA_F32, TSA_BF16 = 0, 1
+
+# Every symbol include/tsa.h declares.
+EXPORTS = ["tsa_status_string", "tsa_last_error", "tsa_version", "tsa_workspace_bytes",
+           "tsa_forward_workspace_bytes", "tsa_score", "tsa_budget", "tsa_select", "tsa_gather",
+           "tsa_attention", "tsa_scatter", "tsa_forward"]
+
+
+class TsaProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("L", ctypes.c_int32), ("d", ctypes.c_int32), ("w", ctypes.c_int32),
+                ("tau", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+_P = ctypes.POINTER(TsaProblem)
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_i32 = ctypes.c_int32
+
+_SIGNATURES = {
+    "tsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "tsa_last_error": (ctypes.c_char_p, []),
+    "tsa_version": (ctypes.c_char_p, []),
+    "tsa_workspace_bytes": (_sz, [_P]),
+    "tsa_forward_workspace_bytes": (_sz, [_P]),
+    "tsa_score": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "tsa_budget": (ctypes.c_int, [_P, _vp, _vp, _vp, _sz, _vp]),
+    "tsa_select": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "tsa_gather": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "tsa_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _i32, _vp, _vp]),
+    "tsa_scatter": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp]),
+    "tsa_forward": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libtsa.so once; raise if it is missing (there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m token_sparse_attention_proxy_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+class TsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load()
+        self.status = status
+        self.name = lib.tsa_status_string(status).decode()
+        self.detail = lib.tsa_last_error().decode()
+        super().__init__(f"{where}: {self.name}: {self.detail}")
+
+
+def check(status: int, where: str) -> None:
+    if status != TSA_OK:
+        raise TsaError(status, where)

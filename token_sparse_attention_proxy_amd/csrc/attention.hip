@@ -1,0 +1,342 @@
+// Causal attention on dense tensors: the attention over the compressed
+// Q, K, V of Token Sparse Attention (gist.science summary, section 2, "Core
+// architecture": the compressed tensors stay dense and contiguous, so an
+// ordinary dense attention kernel runs on them), and, with the GQA head map,
+// the dense baseline over the full sequence.
+//
+//   o[i] = sum_{j<=i} softmax_j(<q_i, k_j>/sqrt(d)) v_j,   i < n
+//
+// bf16 path (gfx950 MFMA, wave64):
+//   * a workgroup owns 128 query rows of one head (4 waves x 32 rows) and
+//     walks 64-key tiles of K and V, double-buffered in LDS;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the A operand is 32 keys
+//     read from LDS, the B operand is the wave's 32 query rows (kept in
+//     registers), so every lane owns one query row and the softmax row
+//     statistics need a single cross-lane exchange (lane l and l^32);
+//   * keys are read into the MFMA rows in a fixed permutation (bits 2 and 3
+//     of the row index swapped) so that the S^T accumulator, converted to
+//     bf16, is directly the B operand of O^T = V^T P^T;
+//   * V is transposed in registers while staged, so LDS holds V^T and the
+//     A operand of the PV product is one 16-byte LDS read per lane;
+//   * online softmax in exp2 units (log2(e)/sqrt(d) folded into one FMA),
+//     fp32 statistics, P rounded to bf16 for the PV product, fp32 output
+//     accumulators, final division and round-to-nearest-even to bf16;
+//   * query blocks are issued heaviest first (the causal triangle).
+// f32 path: a plain fp32 VALU kernel (one query row per thread).
+#include "tsa_device.h"
+#include "tsa_internal.h"
+
+namespace tsa {
+namespace {
+
+// ---------------------------------------------------------------- bf16 MFMA
+constexpr int kThreads = 256;
+constexpr int kBM = 128;          // query rows per workgroup
+constexpr int kBN = 64;           // keys per tile
+constexpr int kKPad = 8;          // bf16 elements of padding per K row in LDS
+constexpr int kVPad = 8;          // bf16 elements of padding per V^T row in LDS
+
+// MFMA row i of a 32-key subtile holds key perm32(i): bits 2 and 3 swapped.
+__device__ __forceinline__ int perm32(int i) {
+  return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+template <int D>
+struct AttnSmem {
+  uint16_t k[2][kBN][D + kKPad];
+  uint16_t vt[2][D][kBN + kVPad];
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ budget,
+    uint16_t* __restrict__ o, int Hq, int Hk, int kv_group, int L, float c) {
+  static_assert(D == 64 || D == 128, "head dim");
+  constexpr int KCH = kBN * D / 8 / kThreads;          // 16-byte K chunks per thread
+  constexpr int VPAIRS = (kBN / 4) * (D / 8);          // (4-key group, 8-d chunk) pairs
+  constexpr int DT = D / 32;                           // 32-wide d tiles of O^T
+  constexpr int KS = D / 16;                           // k-steps of S^T
+  constexpr int NSUB = kBN / 32;                       // 32-key subtiles
+  __shared__ AttnSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int bh = blockIdx.y;
+  const int b = bh / Hq, h = bh % Hq;
+  const int hk = h / kv_group;
+  const int n = budget ? min(max(budget[b], 0), L) : L;
+  const int nqb = (L + kBM - 1) / kBM;
+  const int q0 = (nqb - 1 - int(blockIdx.x)) * kBM;    // heaviest blocks first
+  if (q0 >= n) return;
+
+  const int64_t qbase = int64_t(bh) * L * D;
+  const int64_t kvbase = (int64_t(b) * Hk + hk) * L * D;
+  const int qrow = q0 + 32 * wave + l32;
+
+  // Q^T as the B operand: lane holds q[qrow][16t + 8*half .. +8].
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (qrow < n) raw = *reinterpret_cast<const u32x4*>(q + qbase + int64_t(qrow) * D + 16 * t + 8 * half);
+    qf[t] = __builtin_bit_cast(bf16x8, raw);
+  }
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
+  float m_run = -INFINITY;   // running row max, exp2 units
+  float l_run = 0.f;         // this lane's share of the row sum
+
+  const int kv_end = min(q0 + kBM, n);
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+
+  u32x4 kreg[KCH];
+  u32x4 vreg[4];
+  const int vpair = tid;                 // (key group, d chunk) handled by this thread
+  const int vkg = vpair % (kBN / 4), vdc = vpair / (kBN / 4);
+
+  auto load_tile = [&](int tile) {
+    const int key0 = tile * kBN;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ch = tid + kThreads * i;
+      const int row = ch / (D / 8), col = ch % (D / 8);
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (key0 + row < n) z = *reinterpret_cast<const u32x4*>(k + kvbase + int64_t(key0 + row) * D + col * 8);
+      kreg[i] = z;
+    }
+    if (vpair < VPAIRS) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = key0 + 4 * vkg + r;
+        u32x4 z = {0u, 0u, 0u, 0u};
+        if (key < n) z = *reinterpret_cast<const u32x4*>(v + kvbase + int64_t(key) * D + vdc * 8);
+        vreg[r] = z;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ch = tid + kThreads * i;
+      const int row = ch / (D / 8), col = ch % (D / 8);
+      *reinterpret_cast<u32x4*>(&sm.k[buf][row][col * 8]) = kreg[i];
+    }
+    if (vpair < VPAIRS) {
+      // 4 keys x 8 d  ->  8 rows of V^T, 4 keys each
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t a0 = vreg[0][p], a1 = vreg[1][p], a2 = vreg[2][p], a3 = vreg[3][p];
+        u32x2 lo, hi;
+        lo.x = (a0 & 0xffffu) | (a1 << 16);
+        lo.y = (a2 & 0xffffu) | (a3 << 16);
+        hi.x = (a0 >> 16) | (a1 & 0xffff0000u);
+        hi.y = (a2 >> 16) | (a3 & 0xffff0000u);
+        *reinterpret_cast<u32x2*>(&sm.vt[buf][8 * vdc + 2 * p][4 * vkg]) = lo;
+        *reinterpret_cast<u32x2*>(&sm.vt[buf][8 * vdc + 2 * p + 1][4 * vkg]) = hi;
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  const int wrow_min = q0 + 32 * wave;
+  const int wrow_max = wrow_min + 31;
+  const int krow = perm32(l32);
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    if (tile + 1 < ntiles) load_tile(tile + 1);
+    const int key0 = tile * kBN;
+    if (key0 <= wrow_max) {
+      f32x16 sacc[NSUB];
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[sb][e] = 0.f;
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * sb + krow][16 * t + 8 * half]);
+          sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[sb], 0, 0, 0);
+        }
+      }
+      // scale to exp2 units, causal mask, tile row max
+      const bool diag = key0 + kBN - 1 > wrow_min;
+      float mt = -INFINITY;
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float x = sacc[sb][e] * c;
+          if (diag) {
+            const int key = key0 + 32 * sb + 16 * ((e >> 2) >> 1) + 8 * half + 4 * ((e >> 2) & 1) + (e & 3);
+            if (key > qrow) x = -INFINITY;
+          }
+          sacc[sb][e] = x;
+          mt = fmaxf(mt, x);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = exp2f(m_run - m_new);   // 0 on the first tile (m_run = -inf)
+      m_run = m_new;
+      float ls = 0.f;
+      bf16x8 pb[NSUB * 2];
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          u32x4 pk;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float p0 = exp2f(sacc[sb][8 * tt + 2 * e2] - m_new);
+            const float p1 = exp2f(sacc[sb][8 * tt + 2 * e2 + 1] - m_new);
+            ls += p0 + p1;
+            pk[e2] = pack_bf16x2(p0, p1);
+          }
+          pb[2 * sb + tt] = __builtin_bit_cast(bf16x8, pk);
+        }
+      l_run = l_run * alpha + ls;
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int kk = 0; kk < NSUB * 2; ++kk) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.vt[buf][32 * dt + l32][16 * kk + 8 * half]);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[dt], 0, 0, 0);
+        }
+    }
+    if (tile + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: O = O^T / l, lane holds d = 32dt + 8g + 4*half + {0..3} of its row
+  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l;
+  if (qrow < n) {
+    uint16_t* orow = o + qbase + int64_t(qrow) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 pk;
+        pk.x = pack_bf16x2(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
+        pk.y = pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * g + 4 * half) = pk;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- f32 VALU
+constexpr int kF32Rows = 64;    // query rows per workgroup (one per thread)
+constexpr int kF32Keys = 32;    // keys per LDS tile
+
+template <int D>
+__global__ __launch_bounds__(kF32Rows) void attn_fwd_f32(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const int32_t* __restrict__ budget, float* __restrict__ o, int Hq, int Hk, int kv_group, int L,
+    float c) {
+  __shared__ float ks[kF32Keys][D];
+  __shared__ float vs[kF32Keys][D];
+  const int bh = blockIdx.y;
+  const int b = bh / Hq, h = bh % Hq;
+  const int hk = h / kv_group;
+  const int n = budget ? min(max(budget[b], 0), L) : L;
+  const int nqb = (L + kF32Rows - 1) / kF32Rows;
+  const int q0 = (nqb - 1 - int(blockIdx.x)) * kF32Rows;
+  if (q0 >= n) return;
+  const int i = q0 + threadIdx.x;
+  const int64_t qbase = int64_t(bh) * L * D;
+  const int64_t kvbase = (int64_t(b) * Hk + hk) * L * D;
+  float qr[D], acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    qr[e] = i < n ? q[qbase + int64_t(i) * D + e] : 0.f;
+    acc[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int kv_end = min(q0 + kF32Rows, n);
+  for (int key0 = 0; key0 < kv_end; key0 += kF32Keys) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kF32Keys * D; e += kF32Rows) {
+      const int r = e / D, col = e % D;
+      const bool ok = key0 + r < n;
+      ks[r][col] = ok ? k[kvbase + int64_t(key0 + r) * D + col] : 0.f;
+      vs[r][col] = ok ? v[kvbase + int64_t(key0 + r) * D + col] : 0.f;
+    }
+    __syncthreads();
+    float x[kF32Keys];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < kF32Keys; ++r) {
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) dot = fmaf(qr[e], ks[r][e], dot);
+      x[r] = (key0 + r <= i) ? dot * c : -INFINITY;
+      mt = fmaxf(mt, x[r]);
+    }
+    const float m_new = fmaxf(m, mt);
+    const float alpha = exp2f(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < D; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int r = 0; r < kF32Keys; ++r) {
+      const float p = exp2f(x[r] - m_new);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] = fmaf(p, vs[r][e], acc[e]);
+    }
+    m = m_new;
+  }
+  if (i < n) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < D; ++e) o[qbase + int64_t(i) * D + e] = acc[e] * inv;
+  }
+}
+
+template <int D>
+hipError_t run_bf16(const Shape& sh, const void* q, const void* k, const void* v,
+                    const int32_t* budget, int kv_group, void* o, hipStream_t st) {
+  const float c = kLog2e / sqrtf(float(D));
+  dim3 grid((sh.L + kBM - 1) / kBM, sh.B * sh.Hq);
+  attn_fwd_bf16<D><<<grid, kThreads, 0, st>>>(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), budget, static_cast<uint16_t*>(o), sh.Hq,
+      sh.Hq / kv_group, kv_group, sh.L, c);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t run_f32(const Shape& sh, const void* q, const void* k, const void* v,
+                   const int32_t* budget, int kv_group, void* o, hipStream_t st) {
+  const float c = kLog2e / sqrtf(float(D));
+  dim3 grid((sh.L + kF32Rows - 1) / kF32Rows, sh.B * sh.Hq);
+  attn_fwd_f32<D><<<grid, kF32Rows, 0, st>>>(
+      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+      budget, static_cast<float*>(o), sh.Hq, sh.Hq / kv_group, kv_group, sh.L, c);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const void* v,
+                            const int32_t* budget, int kv_group, void* o, hipStream_t st) {
+  if (sh.dtype == TSA_BF16)
+    return sh.d == 128 ? run_bf16<128>(sh, q, k, v, budget, kv_group, o, st)
+                       : run_bf16<64>(sh, q, k, v, budget, kv_group, o, st);
+  return sh.d == 128 ? run_f32<128>(sh, q, k, v, budget, kv_group, o, st)
+                     : run_f32<64>(sh, q, k, v, budget, kv_group, o, st);
+}
+
+}  // namespace tsa

@@ -1,0 +1,192 @@
+// Global budget: "Dynamic Token Coverage", budget allocation (gist.science
+// summary of Token Sparse Attention, section 2).  Tokens are ordered by
+// ascending importance and the low tail is pruned while the pruned mass
+// stays within tau; the result is one budget shared by every head of the
+// sequence.
+//
+// Importance of token j is the head-mean of the per-head scores.  It is
+// counted exactly: sigma_j = sum_h floor(clip(s,0,1) * 2^50) is a 64-bit
+// integer, so every sum below is exact and independent of reduction order.
+// With C(p) the sum of the p smallest sigma and thr = floor(Hq*tau*2^50):
+//   P = max{p in [0, L-1] : C(p) <= thr},  budget = L - P   (tau = 0: L).
+//
+// The cut is found without sorting: a most-significant-digit radix descent
+// over the sigma values keeps (count, mass) histograms and at each level
+// moves into the first digit bucket where the running mass exceeds thr.  It
+// stops when that bucket holds one value or all bits are fixed; all values
+// left in the bucket are then equal, and P follows in closed form.
+#include "tsa_device.h"
+#include "tsa_internal.h"
+
+namespace tsa {
+namespace {
+
+constexpr int kSigmaThreads = 256;
+constexpr int kCutThreads = 1024;
+constexpr int kDigitBits = 11;
+constexpr int kBuckets = 1 << kDigitBits;
+
+__device__ __forceinline__ uint64_t quantise(float x) {
+  // fmaxf/fminf return the non-NaN operand, so NaN counts as 0.
+  x = fminf(fmaxf(x, 0.0f), 1.0f);
+  return uint64_t(double(x) * 1125899906842624.0);   // * 2^50, exact; truncation = floor
+}
+
+__global__ void clear_u64(uint64_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// sigma[b,j] = sum over query heads, in head order, of the quantised score.
+__global__ __launch_bounds__(kSigmaThreads) void budget_sigma(const float* __restrict__ s,
+                                                              uint64_t* __restrict__ sigma,
+                                                              uint64_t* __restrict__ sigmax,
+                                                              int Hq, int L) {
+  __shared__ uint64_t red[kSigmaThreads / 64];
+  const int b = blockIdx.y;
+  const int j = blockIdx.x * kSigmaThreads + threadIdx.x;
+  uint64_t acc = 0;
+  if (j < L) {
+    const float* sb = s + int64_t(b) * Hq * L + j;
+    for (int h = 0; h < Hq; ++h) acc += quantise(sb[int64_t(h) * L]);
+    sigma[int64_t(b) * L + j] = acc;
+  }
+  // block max, then one integer atomic per block
+  uint64_t m = acc;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t y = __shfl_xor(m, o, 64);
+    m = y > m ? y : m;
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t mm = 0;
+    for (int i = 0; i < kSigmaThreads / 64; ++i) mm = red[i] > mm ? red[i] : mm;
+    atomicMax(reinterpret_cast<unsigned long long*>(sigmax + b), (unsigned long long)mm);
+  }
+}
+
+// One workgroup per sequence: radix descent for the coverage cut.
+__global__ __launch_bounds__(kCutThreads) void budget_cut(const uint64_t* __restrict__ sigma,
+                                                          const uint64_t* __restrict__ sigmax,
+                                                          int32_t* __restrict__ budget, int L,
+                                                          uint64_t thr) {
+  __shared__ uint32_t cnt[kBuckets];
+  __shared__ uint64_t mass[kBuckets];
+  __shared__ uint64_t scan_tmp[17];
+  __shared__ int first_cross;
+  __shared__ uint64_t sh_below_mass, sh_bucket_mass;
+  __shared__ uint32_t sh_below_cnt, sh_bucket_cnt;
+
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const uint64_t* sg = sigma + int64_t(b) * L;
+  const uint64_t maxv = sigmax[b];
+  int lo = maxv ? 64 - __clzll((long long)maxv) : 1;   // bits above `lo` are zero for all values
+  uint64_t prefix = 0;          // value of bits [lo + width, 64) shared by the candidates
+  uint64_t mass_below = 0;      // exact mass of all values below the candidate range
+  uint64_t cnt_below = 0;
+  uint64_t n_eq = 0, T = 0;
+  bool crossed = true;
+
+  while (true) {
+    const int width = lo < kDigitBits ? lo : kDigitBits;
+    lo -= width;
+    const int hi = lo + width;
+    for (int i = t; i < kBuckets; i += kCutThreads) {
+      cnt[i] = 0;
+      mass[i] = 0;
+    }
+    if (t == 0) first_cross = kBuckets;
+    __syncthreads();
+    for (int j = t; j < L; j += kCutThreads) {
+      const uint64_t v = sg[j];
+      const uint64_t top = hi >= 64 ? 0 : (v >> hi);
+      if (top == prefix) {
+        const int dgt = int((v >> lo) & uint64_t(kBuckets - 1));
+        atomicAdd(&cnt[dgt], 1u);
+        atomicAdd(reinterpret_cast<unsigned long long*>(&mass[dgt]), (unsigned long long)v);
+      }
+    }
+    __syncthreads();
+    // Each thread owns two consecutive buckets; exclusive scan of their masses.
+    const int d0 = 2 * t;
+    const uint64_t m0 = mass[d0], m1 = mass[d0 + 1];
+    uint64_t total;
+    const uint64_t excl = block_excl_scan_u64(m0 + m1, scan_tmp, &total);
+    const uint64_t room = thr - mass_below;       // mass_below <= thr holds throughout
+    if (excl + m0 > room) atomicMin(&first_cross, d0);
+    else if (excl + m0 + m1 > room) atomicMin(&first_cross, d0 + 1);
+    __syncthreads();
+    const int dstar = first_cross;
+    if (dstar == kBuckets) {          // the whole candidate range stays within the threshold
+      crossed = false;
+      break;
+    }
+    // Mass of the buckets below d*: the owner of d* knows its prefix.
+    if (t == (dstar >> 1)) {
+      sh_below_mass = excl + ((dstar & 1) ? m0 : 0);
+      sh_bucket_mass = (dstar & 1) ? m1 : m0;
+    }
+    // Count below d*: a second scan over the counts.
+    const uint64_t c01 = uint64_t(cnt[d0]) + cnt[d0 + 1];
+    uint64_t ctot;
+    const uint64_t cex = block_excl_scan_u64(c01, scan_tmp, &ctot);
+    if (t == (dstar >> 1)) {
+      sh_below_cnt = uint32_t(cex + ((dstar & 1) ? cnt[d0] : 0));
+      sh_bucket_cnt = cnt[dstar];
+    }
+    __syncthreads();
+    mass_below += sh_below_mass;
+    cnt_below += sh_below_cnt;
+    n_eq = sh_bucket_cnt;
+    const uint64_t bucket_mass = sh_bucket_mass;
+    prefix = (prefix << width) | uint64_t(dstar);
+    __syncthreads();
+    if (n_eq == 1 || lo == 0) {
+      T = bucket_mass / n_eq;         // all values left in the bucket are equal
+      break;
+    }
+  }
+  if (t == 0) {
+    uint64_t P;
+    if (!crossed) {
+      P = uint64_t(L) - 1;
+    } else {
+      const uint64_t m = (thr - mass_below) / T;
+      P = cnt_below + (m < n_eq - 1 ? m : n_eq - 1);
+      if (P > uint64_t(L) - 1) P = uint64_t(L) - 1;
+    }
+    budget[b] = int32_t(uint64_t(L) - P);
+  }
+}
+
+__global__ void budget_fill(int32_t* __restrict__ budget, int B, int L) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < B) budget[i] = L;
+}
+
+}  // namespace
+
+hipError_t launch_budget(const Shape& sh, const float* scores, int32_t* budget, char* ws,
+                         hipStream_t st) {
+  if (sh.tau == 0.0f) {   // tau = 0 prunes nothing
+    budget_fill<<<(sh.B + 255) / 256, 256, 0, st>>>(budget, sh.B, sh.L);
+    return hipGetLastError();
+  }
+  const StepWs lay = step_ws_layout(sh);
+  uint64_t* sigma = reinterpret_cast<uint64_t*>(ws + lay.sigma);
+  uint64_t* sigmax = reinterpret_cast<uint64_t*>(ws + lay.sigmax);
+  // floor(Hq * tau * 2^50): tau has a 24-bit significand and Hq <= 2^12, so
+  // the product is exact in double.
+  const double x = double(sh.Hq) * double(sh.tau) * 1125899906842624.0;
+  const uint64_t thr = uint64_t(x);
+  clear_u64<<<(sh.B + 255) / 256, 256, 0, st>>>(sigmax, sh.B);
+  budget_sigma<<<dim3((sh.L + kSigmaThreads - 1) / kSigmaThreads, sh.B), kSigmaThreads, 0, st>>>(
+      scores, sigma, sigmax, sh.Hq, sh.L);
+  budget_cut<<<sh.B, kCutThreads, 0, st>>>(sigma, sigmax, budget, sh.L, thr);
+  return hipGetLastError();
+}
+
+}  // namespace tsa

@@ -1,0 +1,112 @@
+// Compression and decompression: "Core architecture", stages 1 and 2
+// (gist.science summary of Token Sparse Attention, section 2).
+//
+// gather:  for i < K_b, qc[b,h,i] = Q[b,h,idx_i]; kc/vc[b,h,i] = K/V[b,g(h),idx_i]
+// scatter: for every j < L, o[b,h,j] = rank_j >= 0 ? oc[b,h,rank_j] : 0
+//
+// Both are pure byte movement: rows are copied as 16-byte vectors, one row
+// per group of lanes.  The scatter is destination-driven, so each output
+// row is written exactly once (copied or zero-filled) and coalesced.
+#include "tsa_device.h"
+#include "tsa_internal.h"
+
+namespace tsa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = 64;
+
+// VPR: 16-byte vectors per row (row bytes / 16).
+template <int VPR>
+__global__ __launch_bounds__(kThreads) void gather_rows(
+    const u32x4* __restrict__ q, const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ budget, u32x4* __restrict__ qc,
+    u32x4* __restrict__ kc, u32x4* __restrict__ vc, int Hq, int Hkv, int L) {
+  constexpr int kRowsPerPass = kThreads / VPR;
+  const int bh = blockIdx.y;
+  const int b = bh / Hq, h = bh % Hq;
+  const int g = h / (Hq / Hkv);
+  const int n = min(max(budget[b], 0), L);
+  const int i0 = blockIdx.x * kRowsPerBlock;
+  if (i0 >= n) return;
+  const int sub = threadIdx.x / VPR, vec = threadIdx.x % VPR;
+  const int64_t hrow = int64_t(bh) * L;                   // first row of (b,h)
+  const int64_t grow = (int64_t(b) * Hkv + g) * L;        // first row of (b,g)
+  for (int i = i0 + sub; i < min(i0 + kRowsPerBlock, n); i += kRowsPerPass) {
+    const int src = idx[hrow + i];
+    const int64_t dst = (hrow + i) * VPR + vec;
+    if (src >= 0 && src < L) {
+      qc[dst] = q[(hrow + src) * VPR + vec];
+      kc[dst] = k[(grow + src) * VPR + vec];
+      vc[dst] = v[(grow + src) * VPR + vec];
+    } else {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      qc[dst] = z;
+      kc[dst] = z;
+      vc[dst] = z;
+    }
+  }
+}
+
+template <int VPR>
+__global__ __launch_bounds__(kThreads) void scatter_rows(const u32x4* __restrict__ oc,
+                                                         const int32_t* __restrict__ rank,
+                                                         u32x4* __restrict__ o, int L) {
+  constexpr int kRowsPerPass = kThreads / VPR;
+  const int bh = blockIdx.y;
+  const int j0 = blockIdx.x * kRowsPerBlock;
+  const int sub = threadIdx.x / VPR, vec = threadIdx.x % VPR;
+  const int64_t hrow = int64_t(bh) * L;
+  for (int j = j0 + sub; j < min(j0 + kRowsPerBlock, L); j += kRowsPerPass) {
+    const int r = rank[hrow + j];
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (r >= 0 && r < L) val = oc[(hrow + r) * VPR + vec];
+    o[(hrow + j) * VPR + vec] = val;
+  }
+}
+
+template <int VPR>
+hipError_t gather_vpr(const Shape& sh, const void* q, const void* k, const void* v,
+                      const int32_t* idx, const int32_t* budget, void* qc, void* kc, void* vc,
+                      hipStream_t st) {
+  dim3 grid((sh.L + kRowsPerBlock - 1) / kRowsPerBlock, sh.B * sh.Hq);
+  gather_rows<VPR><<<grid, kThreads, 0, st>>>(
+      static_cast<const u32x4*>(q), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
+      idx, budget, static_cast<u32x4*>(qc), static_cast<u32x4*>(kc), static_cast<u32x4*>(vc),
+      sh.Hq, sh.Hkv, sh.L);
+  return hipGetLastError();
+}
+
+template <int VPR>
+hipError_t scatter_vpr(const Shape& sh, const void* oc, const int32_t* rank, void* o,
+                       hipStream_t st) {
+  dim3 grid((sh.L + kRowsPerBlock - 1) / kRowsPerBlock, sh.B * sh.Hq);
+  scatter_rows<VPR><<<grid, kThreads, 0, st>>>(static_cast<const u32x4*>(oc), rank,
+                                                static_cast<u32x4*>(o), sh.L);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gather(const Shape& sh, const void* q, const void* k, const void* v,
+                         const int32_t* idx, const int32_t* budget, void* qc, void* kc, void* vc,
+                         hipStream_t st) {
+  switch (sh.row_bytes() / 16) {
+    case 8: return gather_vpr<8>(sh, q, k, v, idx, budget, qc, kc, vc, st);
+    case 16: return gather_vpr<16>(sh, q, k, v, idx, budget, qc, kc, vc, st);
+    case 32: return gather_vpr<32>(sh, q, k, v, idx, budget, qc, kc, vc, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_scatter(const Shape& sh, const void* oc, const int32_t* rank, void* o,
+                          hipStream_t st) {
+  switch (sh.row_bytes() / 16) {
+    case 8: return scatter_vpr<8>(sh, oc, rank, o, st);
+    case 16: return scatter_vpr<16>(sh, oc, rank, o, st);
+    case 32: return scatter_vpr<32>(sh, oc, rank, o, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tsa

@@ -1,0 +1,122 @@
+// Per-head selection: "Dynamic Token Coverage", per-head selection
+// (gist.science summary of Token Sparse Attention, section 2).  With the
+// global budget K fixed, each head independently keeps its own top-K tokens
+// by its own scores.  Order: score descending, then index ascending, so the
+// chosen set is unique.  The set is written in ascending index order (which
+// keeps the causal order of the compressed sequence), with the inverse map.
+//
+// Scores are non-negative floats, so their bit patterns order like the
+// values; NaN and negative values rank as 0.  One workgroup per head:
+//   1. radix descent (11/11/10-bit digits) finds T, the K-th largest key;
+//   2. with c_gt = #{key > T} and need = K - c_gt, token j is kept when
+//      key_j > T, or key_j == T and fewer than `need` T-valued tokens
+//      precede it; one block scan per 1024 tokens of the packed
+//      (greater, equal) counts gives every kept token its output slot.
+// Only integer operations are involved: results are bit-exact and
+// deterministic.
+#include "tsa_device.h"
+#include "tsa_internal.h"
+
+namespace tsa {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kBuckets = 2048;
+
+__device__ __forceinline__ uint32_t score_key(float x) {
+  return (x > 0.0f) ? __float_as_uint(x) : 0u;   // NaN, -0, negatives -> 0
+}
+
+__global__ __launch_bounds__(kThreads) void select_topk(const float* __restrict__ s,
+                                                        const int32_t* __restrict__ budget,
+                                                        int32_t* __restrict__ idx,
+                                                        int32_t* __restrict__ rank, int Hq,
+                                                        int L) {
+  __shared__ uint32_t hist[kBuckets];
+  __shared__ uint64_t scan_tmp[17];
+  __shared__ int dsel;
+  __shared__ uint32_t sh_above;
+  const int bh = blockIdx.x;
+  const int b = bh / Hq;
+  const int t = threadIdx.x;
+  const int K = min(max(budget[b], 0), L);
+  const float* sh = s + int64_t(bh) * L;
+  int32_t* ih = idx + int64_t(bh) * L;
+  int32_t* rh = rank + int64_t(bh) * L;
+
+  // ---- 1. the K-th largest key T
+  uint32_t prefix = 0, above = 0;
+  const int widths[3] = {11, 11, 10};
+  int lo = 32;
+  for (int lev = 0; lev < 3; ++lev) {
+    const int width = widths[lev];
+    const int hi = lo;
+    lo -= width;
+    for (int i = t; i < kBuckets; i += kThreads) hist[i] = 0;
+    if (t == 0) dsel = -1;
+    __syncthreads();
+    for (int j = t; j < L; j += kThreads) {
+      const uint32_t u = score_key(sh[j]);
+      const uint32_t top = hi >= 32 ? 0u : (u >> hi);
+      if (top == prefix) atomicAdd(&hist[(u >> lo) & ((1u << width) - 1u)], 1u);
+    }
+    __syncthreads();
+    // Thread t owns digits dA = 2047-2t and dB = dA-1 (descending order).
+    const int dA = kBuckets - 1 - 2 * t, dB = dA - 1;
+    const uint32_t cA = hist[dA], cB = hist[dB];
+    uint64_t tot;
+    const uint64_t excl = block_excl_scan_u64(uint64_t(cA) + cB, scan_tmp, &tot);
+    // largest digit whose cumulative count from the top reaches K
+    if (uint64_t(above) + excl + cA >= uint64_t(K)) atomicMax(&dsel, dA);
+    else if (uint64_t(above) + excl + cA + cB >= uint64_t(K)) atomicMax(&dsel, dB);
+    __syncthreads();
+    const int d = dsel < 0 ? 0 : dsel;
+    if (t == ((kBuckets - 1 - d) >> 1)) sh_above = above + uint32_t(excl) + ((d == dB) ? cA : 0u);
+    __syncthreads();
+    above = sh_above;
+    prefix = (prefix << width) | uint32_t(d);
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  const uint32_t need = uint32_t(K) - above;   // T-valued tokens to keep, lowest indices first
+
+  // ---- 2. ascending compaction
+  uint32_t carry_gt = 0, carry_eq = 0;
+  for (int base = 0; base < L; base += kThreads) {
+    const int j = base + t;
+    uint32_t gt = 0, eq = 0;
+    if (j < L) {
+      const uint32_t u = score_key(sh[j]);
+      gt = u > T;
+      eq = u == T;
+    }
+    uint64_t tot;
+    const uint64_t ex = block_excl_scan_u64((uint64_t(gt) << 32) | eq, scan_tmp, &tot);
+    const uint32_t gt_before = carry_gt + uint32_t(ex >> 32);
+    const uint32_t eq_before = carry_eq + uint32_t(ex & 0xffffffffu);
+    if (j < L) {
+      const bool keep = gt || (eq && eq_before < need);
+      if (keep) {
+        const uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
+        ih[pos] = j;
+        rh[j] = int32_t(pos);
+      } else {
+        rh[j] = -1;
+      }
+    }
+    carry_gt += uint32_t(tot >> 32);
+    carry_eq += uint32_t(tot & 0xffffffffu);
+  }
+  for (int i = K + t; i < L; i += kThreads) ih[i] = -1;
+}
+
+}  // namespace
+
+hipError_t launch_select(const Shape& sh, const float* scores, const int32_t* budget,
+                         int32_t* idx, int32_t* rank, char* ws, hipStream_t st) {
+  (void)ws;
+  select_topk<<<sh.B * sh.Hq, kThreads, 0, st>>>(scores, budget, idx, rank, sh.Hq, sh.L);
+  return hipGetLastError();
+}
+
+}  // namespace tsa

@@ -1,0 +1,289 @@
+// C ABI of libtsa.so: validation, workspace carving and launch sequencing.
+// Kernels live in the other translation units; see tsa_internal.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "tsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tsa_status fail(tsa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+tsa_status fail(tsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+tsa_status ok() {
+  g_last_error.clear();
+  return TSA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+// Shape checks shared by every entry point.
+tsa_status check_problem(const tsa_problem* p, tsa::Shape* out) {
+  if (!p) return fail(TSA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->L < 1 || p->d < 1 || p->w < 1)
+    return fail(TSA_ERR_INVALID_ARG, "dimensions must be >= 1 (B=%d Hq=%d Hkv=%d L=%d d=%d w=%d)",
+                p->B, p->Hq, p->Hkv, p->L, p->d, p->w);
+  if (p->Hq % p->Hkv != 0)
+    return fail(TSA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", p->Hq, p->Hkv);
+  if (p->w > p->L) return fail(TSA_ERR_INVALID_ARG, "w=%d exceeds L=%d", p->w, p->L);
+  if (p->Hq > tsa::kMaxHq) return fail(TSA_ERR_INVALID_ARG, "Hq=%d exceeds %d", p->Hq, tsa::kMaxHq);
+  if (int64_t(p->L) > tsa::kMaxL) return fail(TSA_ERR_INVALID_ARG, "L=%d exceeds 2^28", p->L);
+  if (std::isnan(p->tau) || !(p->tau >= 0.0f) || !(p->tau < 1.0f))
+    return fail(TSA_ERR_INVALID_ARG, "tau=%g is outside [0, 1)", double(p->tau));
+  if (p->dtype != TSA_F32 && p->dtype != TSA_BF16)
+    return fail(TSA_ERR_UNSUPPORTED, "dtype %d is not supported (TSA_F32=0, TSA_BF16=1)", p->dtype);
+  if (p->d != 64 && p->d != 128)
+    return fail(TSA_ERR_UNSUPPORTED, "head dim d=%d is not supported (64 or 128)", p->d);
+  *out = tsa::Shape{p->B, p->Hq, p->Hkv, p->L, p->d, p->w, p->tau, p->dtype};
+  return TSA_OK;
+}
+
+tsa_status check_ptr(const void* ptr, const char* name) {
+  if (!ptr) return fail(TSA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(TSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return TSA_OK;
+}
+
+tsa_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need)
+    return fail(TSA_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu required", ws_bytes, need);
+  if (need > 0 && (!ws || !aligned256(ws)))
+    return fail(TSA_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  return TSA_OK;
+}
+
+// Host-forceable launch failure, for testing error propagation without a GPU fault.
+bool fault_injected() {
+  const char* e = std::getenv("TSA_FAULT_INJECT");
+  return e && std::strcmp(e, "launch") == 0;
+}
+
+tsa_status launched(hipError_t err, const char* what) {
+  if (err != hipSuccess) return fail(TSA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+  return ok();
+}
+
+tsa_status injected(const char* what) {
+  return fail(TSA_ERR_HIP, "%s: injected launch failure (TSA_FAULT_INJECT)", what);
+}
+
+#define TSA_TRY(expr)                 \
+  do {                                \
+    tsa_status st_ = (expr);          \
+    if (st_ != TSA_OK) return st_;    \
+  } while (0)
+
+}  // namespace
+
+namespace tsa {
+
+StepWs step_ws_layout(const Shape& s) {
+  StepWs w{};
+  size_t off = 0;
+  w.part = off;
+  off = align256(off + sizeof(float) * 2 * size_t(s.B) * s.Hq * s.w * s.n_chunk());
+  w.rowstat = off;
+  off = align256(off + sizeof(float) * 2 * size_t(s.B) * s.Hq * s.w);
+  w.sigma = off;
+  off = align256(off + sizeof(uint64_t) * size_t(s.B) * s.L);
+  w.sigmax = off;
+  off = align256(off + sizeof(uint64_t) * size_t(s.B));
+  w.selstate = off;
+  off = align256(off + sizeof(int32_t) * 4 * size_t(s.B) * s.Hq);
+  w.total = off;
+  return w;
+}
+
+FwdWs fwd_ws_layout(const Shape& s) {
+  FwdWs f{};
+  f.step = step_ws_layout(s);
+  size_t off = f.step.total;
+  const size_t heads = size_t(s.B) * s.Hq;
+  f.scores = off;
+  off = align256(off + sizeof(float) * heads * s.L);
+  f.rank = off;
+  off = align256(off + sizeof(int32_t) * heads * s.L);
+  const size_t tens = heads * size_t(s.L) * size_t(s.row_bytes());
+  f.qc = off;
+  off = align256(off + tens);
+  f.kc = off;
+  off = align256(off + tens);
+  f.vc = off;
+  off = align256(off + tens);
+  f.oc = off;
+  off = align256(off + tens);
+  f.total = off;
+  return f;
+}
+
+}  // namespace tsa
+
+extern "C" {
+
+const char* tsa_status_string(tsa_status st) {
+  switch (st) {
+    case TSA_OK: return "TSA_OK";
+    case TSA_ERR_INVALID_ARG: return "TSA_ERR_INVALID_ARG";
+    case TSA_ERR_UNSUPPORTED: return "TSA_ERR_UNSUPPORTED";
+    case TSA_ERR_WORKSPACE: return "TSA_ERR_WORKSPACE";
+    case TSA_ERR_HIP: return "TSA_ERR_HIP";
+  }
+  return "TSA_ERR_UNKNOWN";
+}
+
+const char* tsa_last_error(void) { return g_last_error.c_str(); }
+
+const char* tsa_version(void) { return "tsa 0.1 gfx950"; }
+
+size_t tsa_workspace_bytes(const tsa_problem* prob) {
+  tsa::Shape s;
+  if (check_problem(prob, &s) != TSA_OK) return 0;
+  return tsa::step_ws_layout(s).total;
+}
+
+size_t tsa_forward_workspace_bytes(const tsa_problem* prob) {
+  tsa::Shape s;
+  if (check_problem(prob, &s) != TSA_OK) return 0;
+  return tsa::fwd_ws_layout(s).total;
+}
+
+tsa_status tsa_score(const tsa_problem* prob, const void* q, const void* k, float* s, void* ws,
+                     size_t ws_bytes, void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_problem(prob, &sh));
+  TSA_TRY(check_ptr(q, "q"));
+  TSA_TRY(check_ptr(k, "k"));
+  TSA_TRY(check_ptr(s, "s"));
+  TSA_TRY(check_ws(ws, ws_bytes, tsa::step_ws_layout(sh).total));
+  if (fault_injected()) return injected("tsa_score");
+  return launched(tsa::launch_score(sh, q, k, s, static_cast<char*>(ws), hipStream_t(stream)),
+                  "tsa_score");
+}
+
+tsa_status tsa_budget(const tsa_problem* prob, const float* s, int32_t* budget, void* ws,
+                      size_t ws_bytes, void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_problem(prob, &sh));
+  TSA_TRY(check_ptr(s, "s"));
+  TSA_TRY(check_ptr(budget, "budget"));
+  TSA_TRY(check_ws(ws, ws_bytes, tsa::step_ws_layout(sh).total));
+  if (fault_injected()) return injected("tsa_budget");
+  return launched(tsa::launch_budget(sh, s, budget, static_cast<char*>(ws), hipStream_t(stream)),
+                  "tsa_budget");
+}
+
+tsa_status tsa_select(const tsa_problem* prob, const float* s, const int32_t* budget, int32_t* idx,
+                      int32_t* rank, void* ws, size_t ws_bytes, void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_problem(prob, &sh));
+  TSA_TRY(check_ptr(s, "s"));
+  TSA_TRY(check_ptr(budget, "budget"));
+  TSA_TRY(check_ptr(idx, "idx"));
+  TSA_TRY(check_ptr(rank, "rank"));
+  TSA_TRY(check_ws(ws, ws_bytes, tsa::step_ws_layout(sh).total));
+  if (fault_injected()) return injected("tsa_select");
+  return launched(
+      tsa::launch_select(sh, s, budget, idx, rank, static_cast<char*>(ws), hipStream_t(stream)),
+      "tsa_select");
+}
+
+tsa_status tsa_gather(const tsa_problem* prob, const void* q, const void* k, const void* v,
+                      const int32_t* idx, const int32_t* budget, void* qc, void* kc, void* vc,
+                      void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_problem(prob, &sh));
+  TSA_TRY(check_ptr(q, "q"));
+  TSA_TRY(check_ptr(k, "k"));
+  TSA_TRY(check_ptr(v, "v"));
+  TSA_TRY(check_ptr(idx, "idx"));
+  TSA_TRY(check_ptr(budget, "budget"));
+  TSA_TRY(check_ptr(qc, "qc"));
+  TSA_TRY(check_ptr(kc, "kc"));
+  TSA_TRY(check_ptr(vc, "vc"));
+  if (fault_injected()) return injected("tsa_gather");
+  return launched(tsa::launch_gather(sh, q, k, v, idx, budget, qc, kc, vc, hipStream_t(stream)),
+                  "tsa_gather");
+}
+
+tsa_status tsa_attention(const tsa_problem* prob, const void* q, const void* k, const void* v,
+                         const int32_t* budget, int32_t kv_group, void* o, void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_problem(prob, &sh));
+  TSA_TRY(check_ptr(q, "q"));
+  TSA_TRY(check_ptr(k, "k"));
+  TSA_TRY(check_ptr(v, "v"));
+  TSA_TRY(check_ptr(o, "o"));
+  if (budget && !aligned16(budget)) return fail(TSA_ERR_INVALID_ARG, "budget is not 16-byte aligned");
+  if (kv_group < 1 || sh.Hq % kv_group != 0)
+    return fail(TSA_ERR_INVALID_ARG, "kv_group=%d must be >= 1 and divide Hq=%d", kv_group, sh.Hq);
+  if (fault_injected()) return injected("tsa_attention");
+  return launched(tsa::launch_attention(sh, q, k, v, budget, kv_group, o, hipStream_t(stream)),
+                  "tsa_attention");
+}
+
+tsa_status tsa_scatter(const tsa_problem* prob, const void* oc, const int32_t* rank, void* o,
+                       void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_problem(prob, &sh));
+  TSA_TRY(check_ptr(oc, "oc"));
+  TSA_TRY(check_ptr(rank, "rank"));
+  TSA_TRY(check_ptr(o, "o"));
+  if (fault_injected()) return injected("tsa_scatter");
+  return launched(tsa::launch_scatter(sh, oc, rank, o, hipStream_t(stream)), "tsa_scatter");
+}
+
+tsa_status tsa_forward(const tsa_problem* prob, const void* q, const void* k, const void* v, void* o,
+                       int32_t* budget, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_problem(prob, &sh));
+  TSA_TRY(check_ptr(q, "q"));
+  TSA_TRY(check_ptr(k, "k"));
+  TSA_TRY(check_ptr(v, "v"));
+  TSA_TRY(check_ptr(o, "o"));
+  TSA_TRY(check_ptr(budget, "budget"));
+  TSA_TRY(check_ptr(idx, "idx"));
+  const tsa::FwdWs f = tsa::fwd_ws_layout(sh);
+  TSA_TRY(check_ws(ws, ws_bytes, f.total));
+  if (fault_injected()) return injected("tsa_forward");
+  char* base = static_cast<char*>(ws);
+  hipStream_t st = hipStream_t(stream);
+  float* scores = reinterpret_cast<float*>(base + f.scores);
+  int32_t* rank = reinterpret_cast<int32_t*>(base + f.rank);
+  void* qc = base + f.qc;
+  void* kc = base + f.kc;
+  void* vc = base + f.vc;
+  void* oc = base + f.oc;
+  hipError_t err;
+  if ((err = tsa::launch_score(sh, q, k, scores, base, st)) != hipSuccess)
+    return launched(err, "tsa_forward/score");
+  if ((err = tsa::launch_budget(sh, scores, budget, base, st)) != hipSuccess)
+    return launched(err, "tsa_forward/budget");
+  if ((err = tsa::launch_select(sh, scores, budget, idx, rank, base, st)) != hipSuccess)
+    return launched(err, "tsa_forward/select");
+  if ((err = tsa::launch_gather(sh, q, k, v, idx, budget, qc, kc, vc, st)) != hipSuccess)
+    return launched(err, "tsa_forward/gather");
+  if ((err = tsa::launch_attention(sh, qc, kc, vc, budget, 1, oc, st)) != hipSuccess)
+    return launched(err, "tsa_forward/attention");
+  if ((err = tsa::launch_scatter(sh, oc, rank, o, st)) != hipSuccess)
+    return launched(err, "tsa_forward/scatter");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Internal declarations shared by the HIP translation units of libtsa.so.
+// Not installed; the public interface is include/tsa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tsa.h"
+
+namespace tsa {
+
+// ---------------------------------------------------------------- constants
+constexpr int kScoreFracBits = 50;     // budget masses are counted in units of 2^-50
+constexpr int kScoreChunk = 256;       // keys per proxy-scoring workgroup
+constexpr int kMaxHq = 4096;           // keeps the budget's integer masses below 2^63
+constexpr int64_t kMaxL = int64_t(1) << 28;
+
+// ---------------------------------------------------------------- shapes
+struct Shape {
+  int B, Hq, Hkv, L, d, w;
+  float tau;
+  int dtype;          // TSA_F32 / TSA_BF16
+  int G() const { return Hq / Hkv; }
+  int eb() const { return dtype == TSA_BF16 ? 2 : 4; }
+  int64_t row_bytes() const { return int64_t(d) * eb(); }
+  int n_chunk() const { return (L + kScoreChunk - 1) / kScoreChunk; }
+};
+
+// Step-scratch layout (offsets in bytes from the workspace base, 256-aligned).
+struct StepWs {
+  size_t part;        // float2 [B*Hq*w*n_chunk]: per-chunk (max, sum) of each proxy row
+  size_t rowstat;     // float2 [B*Hq*w]: (max in exp2 units, 1/Z) of each proxy row
+  size_t sigma;       // uint64 [B*L]: head-summed quantised masses
+  size_t sigmax;      // uint64 [B]: max sigma per sequence
+  size_t selstate;    // int32 [B*Hq*4]: per-head selection threshold state
+  size_t total;
+};
+StepWs step_ws_layout(const Shape& s);
+
+// Forward-scratch layout: step scratch first, then the intermediates.
+struct FwdWs {
+  StepWs step;
+  size_t scores;      // float [B*Hq*L]
+  size_t rank;        // int32 [B*Hq*L]
+  size_t qc, kc, vc, oc;   // dtype [B*Hq*L*d] each
+  size_t total;
+};
+FwdWs fwd_ws_layout(const Shape& s);
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipGetLastError() after enqueueing its kernels on `st`.
+hipError_t launch_score(const Shape& s, const void* q, const void* k, float* scores,
+                        char* ws, hipStream_t st);
+hipError_t launch_budget(const Shape& s, const float* scores, int32_t* budget, char* ws,
+                         hipStream_t st);
+hipError_t launch_select(const Shape& s, const float* scores, const int32_t* budget,
+                         int32_t* idx, int32_t* rank, char* ws, hipStream_t st);
+hipError_t launch_gather(const Shape& s, const void* q, const void* k, const void* v,
+                         const int32_t* idx, const int32_t* budget, void* qc, void* kc,
+                         void* vc, hipStream_t st);
+hipError_t launch_attention(const Shape& s, const void* q, const void* k, const void* v,
+                            const int32_t* budget, int kv_group, void* o, hipStream_t st);
+hipError_t launch_scatter(const Shape& s, const void* oc, const int32_t* rank, void* o,
+                          hipStream_t st);
+
+}  // namespace tsa

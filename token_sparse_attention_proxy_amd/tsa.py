@@ -1,0 +1,164 @@
+"""Python binding of libtsa.so with the same entry-point names as include/tsa.h.
+
+PyTorch provides device memory and the stream handle; the wrappers only
+allocate outputs, pass raw pointers and check the status code.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import TSA_BF16, TSA_F32, TsaError, TsaProblem, check
+
+_DTYPES = {"f32": (TSA_F32, torch.float32), "bf16": (TSA_BF16, torch.bfloat16)}
+
+
+@dataclasses.dataclass(frozen=True)
+class Problem:
+    B: int
+    Hq: int
+    Hkv: int
+    L: int
+    d: int
+    w: int
+    tau: float
+    dtype: str = "bf16"          # "f32" or "bf16"
+
+    @classmethod
+    def from_qkv(cls, q: torch.Tensor, k: torch.Tensor, w: int, tau: float) -> "Problem":
+        B, Hq, L, d = q.shape
+        dt = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(q.dtype)
+        if dt is None:
+            raise TypeError(f"unsupported dtype {q.dtype}")
+        return cls(B, Hq, k.shape[1], L, d, w, float(tau), dt)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _DTYPES[self.dtype][1]
+
+    def c(self) -> TsaProblem:
+        code = _DTYPES[self.dtype][0] if self.dtype in _DTYPES else 99
+        return TsaProblem(self.B, self.Hq, self.Hkv, self.L, self.d, self.w, self.tau, code)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live in device memory")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _empty(shape, dtype, like: torch.Tensor) -> torch.Tensor:
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def workspace_bytes(prob: Problem) -> int:
+    return int(_lib.load().tsa_workspace_bytes(ctypes.byref(prob.c())))
+
+
+def forward_workspace_bytes(prob: Problem) -> int:
+    return int(_lib.load().tsa_forward_workspace_bytes(ctypes.byref(prob.c())))
+
+
+def _ws(prob: Problem, like: torch.Tensor, ws: Optional[torch.Tensor], nbytes: int) -> torch.Tensor:
+    if ws is None:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=like.device)
+    return ws
+
+
+def tsa_score(prob: Problem, q, k, s=None, ws=None):
+    lib = _lib.load()
+    p = prob.c()
+    if s is None:
+        s = _empty((prob.B, prob.Hq, prob.L), torch.float32, q)
+    ws = _ws(prob, q, ws, workspace_bytes(prob))
+    check(lib.tsa_score(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(s), _ptr(ws), ws.numel(),
+                        _stream(q.device)), "tsa_score")
+    return s
+
+
+def tsa_budget(prob: Problem, s, budget=None, ws=None):
+    lib = _lib.load()
+    p = prob.c()
+    if budget is None:
+        budget = _empty((prob.B,), torch.int32, s)
+    ws = _ws(prob, s, ws, workspace_bytes(prob))
+    check(lib.tsa_budget(ctypes.byref(p), _ptr(s), _ptr(budget), _ptr(ws), ws.numel(),
+                         _stream(s.device)), "tsa_budget")
+    return budget
+
+
+def tsa_select(prob: Problem, s, budget, idx=None, rank=None, ws=None):
+    lib = _lib.load()
+    p = prob.c()
+    shape = (prob.B, prob.Hq, prob.L)
+    idx = _empty(shape, torch.int32, s) if idx is None else idx
+    rank = _empty(shape, torch.int32, s) if rank is None else rank
+    ws = _ws(prob, s, ws, workspace_bytes(prob))
+    check(lib.tsa_select(ctypes.byref(p), _ptr(s), _ptr(budget), _ptr(idx), _ptr(rank), _ptr(ws),
+                         ws.numel(), _stream(s.device)), "tsa_select")
+    return idx, rank
+
+
+def tsa_gather(prob: Problem, q, k, v, idx, budget, qc=None, kc=None, vc=None):
+    lib = _lib.load()
+    p = prob.c()
+    shape = (prob.B, prob.Hq, prob.L, prob.d)
+    qc = _empty(shape, q.dtype, q) if qc is None else qc
+    kc = _empty(shape, q.dtype, q) if kc is None else kc
+    vc = _empty(shape, q.dtype, q) if vc is None else vc
+    check(lib.tsa_gather(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(budget),
+                         _ptr(qc), _ptr(kc), _ptr(vc), _stream(q.device)), "tsa_gather")
+    return qc, kc, vc
+
+
+def tsa_attention(prob: Problem, q, k, v, budget=None, kv_group: int = 1, o=None):
+    lib = _lib.load()
+    p = prob.c()
+    o = _empty(q.shape, q.dtype, q) if o is None else o
+    check(lib.tsa_attention(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(budget), kv_group,
+                            _ptr(o), _stream(q.device)), "tsa_attention")
+    return o
+
+
+def tsa_scatter(prob: Problem, oc, rank, o=None):
+    lib = _lib.load()
+    p = prob.c()
+    o = _empty(oc.shape, oc.dtype, oc) if o is None else o
+    check(lib.tsa_scatter(ctypes.byref(p), _ptr(oc), _ptr(rank), _ptr(o), _stream(oc.device)),
+          "tsa_scatter")
+    return o
+
+
+def tsa_forward(prob: Problem, q, k, v, o=None, budget=None, idx=None, ws=None):
+    lib = _lib.load()
+    p = prob.c()
+    o = _empty(q.shape, q.dtype, q) if o is None else o
+    budget = _empty((prob.B,), torch.int32, q) if budget is None else budget
+    idx = _empty((prob.B, prob.Hq, prob.L), torch.int32, q) if idx is None else idx
+    ws = _ws(prob, q, ws, forward_workspace_bytes(prob))
+    check(lib.tsa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(budget),
+                          _ptr(idx), _ptr(ws), ws.numel(), _stream(q.device)), "tsa_forward")
+    return o, budget, idx
+
+
+def forward(q, k, v, w: int, tau: float):
+    """The whole op on torch device tensors: returns (o, budget, idx)."""
+    prob = Problem.from_qkv(q, k, w, tau)
+    return tsa_forward(prob, q, k, v)
+
+
+__all__ = ["Problem", "TsaError", "workspace_bytes", "forward_workspace_bytes", "tsa_score",
+           "tsa_budget", "tsa_select", "tsa_gather", "tsa_attention", "tsa_scatter",
+           "tsa_forward", "forward"]
