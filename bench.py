@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the Token Sparse Attention prefill op on one MI355X.
+
+One step = one tsa_forward over one batch (score -> budget -> select ->
+gather -> causal attention -> scatter) on seeded synthetic Q, K, V that are
+already resident in HBM.  Printed as one JSON line, with:
+  * the dense causal attention baseline (same attention kernel, GQA head map,
+    no gather / scatter) and the speedup against it;
+  * a per-step breakdown timed with HIP events on the launch stream, and the
+    roofline of the dominant kernel (the attention) from that timed region;
+  * the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TSA attention ms/layer at 128K bf16; speedup vs own dense; % MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3          # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+ATTN_SRC = os.path.join(ROOT, "token_sparse_attention_proxy_amd", "csrc", "attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attention_flops(budget, Hq: int, d: int) -> float:
+    """Algorithmic FLOPs of causal attention over K_b rows: 4d per visible (i, j) pair."""
+    return float(sum(2.0 * d * int(K) * (int(K) + 1) * Hq for K in budget))
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counters, if they match this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tab = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = tab.get(kernel, {}).get(workload)
+    if not ent or ent.get("source_sha") != source_hash(ATTN_SRC):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, q, k, v, tau, K_gpu: int):
+    """The fp64 oracle, as it stands, on a bounded sample; scaled to ms/layer."""
+    from threadpoolctl import threadpool_info
+    from oracle import tsa_oracle as O
+
+    B, Hq, Hkv, L, d = wl.B, wl.Hq, wl.Hkv, wl.L, wl.d
+    t0 = time.perf_counter()
+    s = O.proxy_scores(q, k, wl.w)
+    t_score = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    budget = O.coverage_budget(s, tau)
+    t_budget = time.perf_counter() - t0
+    # per-head steps on head (0, 0), scaled by the number of heads
+    K = int(budget[0])
+    t0 = time.perf_counter()
+    idx, _ = O.select_heads(s[:1, :1], budget[:1])
+    t_select = (time.perf_counter() - t0) * B * Hq
+    t0 = time.perf_counter()
+    qc, kc, vc = O.gather(q[:1, :1], k[:1, :1], v[:1, :1], idx, budget[:1])
+    t_gather = (time.perf_counter() - t0) * B * Hq
+    # attention on the last rows of the compact sequence (the most expensive ones)
+    n_rows = min(K, 1024 if L >= 65536 else 2048)
+    rows = np.arange(K - n_rows, K)
+    t0 = time.perf_counter()
+    oc_rows = O.causal_attention(qc[0, 0, :K], kc[0, 0, :K], vc[0, 0, :K], rows=rows)
+    t_attn_sample = time.perf_counter() - t0
+    pairs_sample = float(np.sum(rows + 1))
+    pairs_layer = float(sum(int(kb) * (int(kb) + 1) // 2 for kb in budget)) * Hq
+    t_attn = t_attn_sample * pairs_layer / pairs_sample
+    oc = np.zeros((1, 1, L, d))
+    oc[0, 0, rows] = oc_rows
+    t0 = time.perf_counter()
+    O.scatter(oc, idx, budget[:1])
+    t_scatter = (time.perf_counter() - t0) * B * Hq
+    total = t_score + t_budget + t_select + t_gather + t_attn + t_scatter
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": round(total * 1e3, 1), "unit": "ms/layer", "cores": int(threads), "kind": "oracle",
+        "sample": (f"fp64 oracle: scores+budget for all {B * Hq} heads in full; select, gather "
+                   f"and scatter of head (0,0) x{B * Hq}; attention of the last {n_rows} compact "
+                   f"rows of head (0,0) (K={K}) scaled by causal pairs x{pairs_layer / pairs_sample:.0f}"),
+        "measured_s": round(t_score + t_budget + t_select / (B * Hq) + t_gather / (B * Hq)
+                            + t_attn_sample + t_scatter / (B * Hq), 2),
+        "budget_matches_gpu": bool(int(budget[0]) == K_gpu),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_bf16_L128k")
+    ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the op runs on a single MI355X; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from token_sparse_attention_proxy_amd import inputs
+    from token_sparse_attention_proxy_amd import tsa as T
+
+    wl = inputs.WORKLOADS[args.workload]
+    tau = float(wl.taus[0] if args.tau is None else args.tau)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {wl.name} tau={tau}: generating inputs")
+    q, k, v = inputs.make_qkv(wl)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(x).to(tdt).to(dev) for x in (q, k, v))
+    if args.no_cpu_baseline:
+        del q, k, v
+    prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, tau, wl.dtype)
+    shape = (wl.B, wl.Hq, wl.L, wl.d)
+    o = torch.empty(shape, dtype=tdt, device=dev)
+    budget = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+    idx = torch.empty((wl.B, wl.Hq, wl.L), dtype=torch.int32, device=dev)
+    ws = torch.empty(T.forward_workspace_bytes(prob), dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream(dev)
+
+    # ---- headline: K timed steps of the fused forward
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        T.tsa_forward(prob, qd, kd, vd, o, budget, idx, ws)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        T.tsa_forward(prob, qd, kd, vd, o, budget, idx, ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    bud = budget.cpu().numpy()
+    log(f"[bench] tsa_forward {ms_step:.3f} ms/step, budget {bud} K/L {bud / wl.L}")
+
+    # ---- per-step breakdown: the same kernels called one by one, HIP events between them
+    heads = wl.B * wl.Hq
+    step_ws = torch.empty(T.workspace_bytes(prob), dtype=torch.uint8, device=dev)
+    s = torch.empty((wl.B, wl.Hq, wl.L), dtype=torch.float32, device=dev)
+    rank = torch.empty_like(idx)
+    qc, kc, vc, oc = (torch.empty(shape, dtype=tdt, device=dev) for _ in range(4))
+    names = ["score", "budget", "select", "gather", "attention", "scatter"]
+    acc = {n: 0.0 for n in names}
+    reps = max(3, min(args.steps, 10))
+    for rep in range(reps + 1):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        ev[0].record(st)
+        T.tsa_score(prob, qd, kd, s, step_ws)
+        ev[1].record(st)
+        T.tsa_budget(prob, s, budget, step_ws)
+        ev[2].record(st)
+        T.tsa_select(prob, s, budget, idx, rank, step_ws)
+        ev[3].record(st)
+        T.tsa_gather(prob, qd, kd, vd, idx, budget, qc, kc, vc)
+        ev[4].record(st)
+        T.tsa_attention(prob, qc, kc, vc, budget, 1, oc)
+        ev[5].record(st)
+        T.tsa_scatter(prob, oc, rank, o)
+        ev[6].record(st)
+        torch.cuda.synchronize()
+        if rep > 0:       # first pass is a warm-up
+            for i, n in enumerate(names):
+                acc[n] += ev[i].elapsed_time(ev[i + 1])
+    steps_ms = {n: acc[n] / reps for n in names}
+    log("[bench] steps ms: " + ", ".join(f"{n} {steps_ms[n]:.3f}" for n in names))
+
+    # ---- dense causal attention baseline (same kernel, GQA head map)
+    dense_ms = None
+    if not args.no_dense:
+        od = torch.empty(shape, dtype=tdt, device=dev)
+        for _ in range(max(1, args.warmup)):
+            T.tsa_attention(prob, qd, kd, vd, None, wl.G, od)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dreps = max(2, min(args.steps, 5))
+        e0.record(st)
+        for _ in range(dreps):
+            T.tsa_attention(prob, qd, kd, vd, None, wl.G, od)
+        e1.record(st)
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / dreps
+        del od
+        log(f"[bench] dense attention {dense_ms:.3f} ms")
+
+    # ---- roofline of the dominant kernel (attention), algorithmic FLOPs
+    bf16 = wl.dtype == "bf16"
+    flops = attention_flops(bud, wl.Hq, wl.d)
+    achieved = flops / (steps_ms["attention"] * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    traffic = measured_traffic("attn_fwd_bf16", wl.name) if bf16 else None
+    roofline = {"bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic, "kernel": "attn_fwd_bf16" if bf16 else "attn_fwd_f32",
+                "flops_per_launch": flops, "avg_launch_ms": round(steps_ms["attention"], 4)}
+
+    # HBM fractions of the byte-moving steps (algorithmic bytes)
+    eb = 2 if bf16 else 4
+    idx_np = idx.cpu().numpy()
+    uniq = 0
+    for b in range(wl.B):
+        for g in range(wl.Hkv):
+            hs = range(g * wl.G, (g + 1) * wl.G)
+            uniq += len(np.unique(np.concatenate([idx_np[b, h, :bud[b]] for h in hs])))
+    Ksum = float(sum(int(x) for x in bud)) * wl.Hq
+    row = wl.d * eb
+    hbm_bytes = {
+        "score": wl.B * wl.Hkv * wl.L * row + heads * wl.w * row + 4 * heads * wl.L,
+        "budget": 4 * heads * wl.L,
+        "select": 4 * heads * wl.L + 4 * Ksum + 4 * heads * wl.L,
+        "gather": Ksum * row + 2 * uniq * row + 3 * Ksum * row + 4 * Ksum,
+        "scatter": Ksum * row + heads * wl.L * row + 4 * heads * wl.L,
+    }
+    kernels = {n: {"ms": round(steps_ms[n], 4),
+                   "GB_s": round(hbm_bytes[n] / (steps_ms[n] * 1e-3) / 1e9, 1),
+                   "hbm_frac": round(hbm_bytes[n] / (steps_ms[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                   "algorithmic_bytes": int(hbm_bytes[n])} for n in hbm_bytes}
+    kernels["attention"] = {"ms": round(steps_ms["attention"], 4),
+                            "TFLOP_s": round(achieved, 2), "mfma_frac": round(achieved / peak, 4)}
+    overhead = sum(steps_ms[n] for n in names if n != "attention")
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms_step, 4),
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "L": wl.L,
+                   "d": wl.d, "w": wl.w, "tau": tau, "global_batch": wl.B, "seq_len": wl.L,
+                   "parallelism": "none"},
+        "budget": [int(x) for x in bud],
+        "keep_frac": [round(int(x) / wl.L, 5) for x in bud],
+        "dense_ms": None if dense_ms is None else round(dense_ms, 4),
+        "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 4),
+        "attention_speedup_vs_dense": None if dense_ms is None else round(dense_ms / steps_ms["attention"], 4),
+        "overhead_share": round(overhead / steps_ms["attention"], 4),
+        "steps_ms": {n: round(steps_ms[n], 4) for n in names},
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle on a bounded sample)")
+        out["cpu_baseline"] = cpu_baseline(wl, q, k, v, tau, int(bud[0]))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
