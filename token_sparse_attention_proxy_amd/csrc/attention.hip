@@ -7,20 +7,32 @@
 //   o[i] = sum_{j<=i} softmax_j(<q_i, k_j>/sqrt(d)) v_j,   i < n
 //
 // bf16 path (gfx950 MFMA, wave64):
-//   * a workgroup owns 128 query rows of one head (4 waves x 32 rows) and
-//     walks 64-key tiles of K and V, double-buffered in LDS;
+//   * a workgroup owns 256 query rows of one head (8 waves x 32 rows, two
+//     waves per SIMD) and walks 64-key tiles of K and V, double-buffered in
+//     LDS;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the A operand is 32 keys
-//     read from LDS, the B operand is the wave's 32 query rows (kept in
-//     registers), so every lane owns one query row and the softmax row
-//     statistics need a single cross-lane exchange (lane l and l^32);
+//     read from LDS, the B operand is the wave's 32 query rows kept in
+//     registers, so every lane owns one query row;
 //   * keys are read into the MFMA rows in a fixed permutation (bits 2 and 3
 //     of the row index swapped) so that the S^T accumulator, converted to
 //     bf16, is directly the B operand of O^T = V^T P^T;
 //   * V is transposed in registers while staged, so LDS holds V^T and the
 //     A operand of the PV product is one 16-byte LDS read per lane;
-//   * online softmax in exp2 units (log2(e)/sqrt(d) folded into one FMA),
-//     fp32 statistics, P rounded to bf16 for the PV product, fp32 output
-//     accumulators, final division and round-to-nearest-even to bf16;
+//   * softmax with a fixed per-row reference: p = exp2(S log2(e)/sqrt(d) - m)
+//     where m is the row max over the first key tile.  The loop then needs
+//     no running max, no cross-lane reduction and no rescaling of O, which
+//     stays in accumulator registers touched only by MFMA: one FMA, one
+//     exp2, one add and half a bf16 pack per score.  Softmax is invariant
+//     to the reference, so the result equals the usual one up to rounding.
+//     A row sum above 2^64 (a later logit far above the first tile's max)
+//     makes the workgroup recompute with the exact row max as reference, so
+//     nothing can overflow;
+//   * P rounded to bf16 for the PV product, fp32 output accumulators, final
+//     division and round-to-nearest-even to bf16;
+//   * loads and stores go through buffer resources sized to the n valid
+//     rows: out-of-range rows read as 0 and are never written, without
+//     branches;
+//   * only each wave's diagonal tile is masked; tiles above it are skipped;
 //   * query blocks are issued heaviest first (the causal triangle).
 // f32 path: a plain fp32 VALU kernel (one query row per thread).
 #include "tsa_device.h"
@@ -30,15 +42,36 @@ namespace tsa {
 namespace {
 
 // ---------------------------------------------------------------- bf16 MFMA
-constexpr int kThreads = 256;
-constexpr int kBM = 128;          // query rows per workgroup
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per workgroup: 32 per wave
 constexpr int kBN = 64;           // keys per tile
 constexpr int kKPad = 8;          // bf16 elements of padding per K row in LDS
 constexpr int kVPad = 8;          // bf16 elements of padding per V^T row in LDS
+// A row sum above 2^64 means some exponent relative to the reference max
+// may have overflowed or lost range: the workgroup then recomputes with the
+// exact row max as reference.
+constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
 
 // MFMA row i of a 32-key subtile holds key perm32(i): bits 2 and 3 swapped.
 __device__ __forceinline__ int perm32(int i) {
   return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+// Buffer resource over `bytes` bytes from `p`: loads past the end return 0,
+// stores past the end are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, int(bytes), 0x00020000);
+}
+
+// max / sum of x[l] and x[l ^ 32] in every lane l.
+__device__ __forceinline__ float max_halves(float x) {
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 template <int D>
@@ -47,8 +80,13 @@ struct AttnSmem {
   uint16_t vt[2][D][kBN + kVPad];
 };
 
+// Key index held in element e of the S^T accumulator of a 32-key subtile, for a lane in `half`.
+__device__ __forceinline__ int acc_key(int e, int half) {
+  return 16 * (e >> 3) + 8 * half + 4 * ((e >> 2) & 1) + (e & 3);
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ budget,
     uint16_t* __restrict__ o, int Hq, int Hk, int kv_group, int L, float c) {
@@ -58,6 +96,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(
   constexpr int DT = D / 32;                           // 32-wide d tiles of O^T
   constexpr int KS = D / 16;                           // k-steps of S^T
   constexpr int NSUB = kBN / 32;                       // 32-key subtiles
+  static_assert(KCH >= 1 && VPAIRS <= kThreads, "tile shape");
   __shared__ AttnSmem<D> sm;
 
   const int tid = threadIdx.x;
@@ -71,34 +110,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(
   const int q0 = (nqb - 1 - int(blockIdx.x)) * kBM;    // heaviest blocks first
   if (q0 >= n) return;
 
-  const int64_t qbase = int64_t(bh) * L * D;
-  const int64_t kvbase = (int64_t(b) * Hk + hk) * L * D;
-  const int qrow = q0 + 32 * wave + l32;
+  const uint32_t head_bytes = uint32_t(n) * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + int64_t(bh) * L * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (int64_t(b) * Hk + hk) * L * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + (int64_t(b) * Hk + hk) * L * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + int64_t(bh) * L * D, head_bytes);
+  const int wr0 = q0 + 32 * wave;            // first query row of this wave
+  const int qrow = wr0 + l32;                // the row this lane owns
+  const int wdiag = wr0 / kBN;               // tile holding this wave's diagonal
 
   // Q^T as the B operand: lane holds q[qrow][16t + 8*half .. +8].
   bf16x8 qf[KS];
 #pragma unroll
-  for (int t = 0; t < KS; ++t) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (qrow < n) raw = *reinterpret_cast<const u32x4*>(q + qbase + int64_t(qrow) * D + 16 * t + 8 * half);
-    qf[t] = __builtin_bit_cast(bf16x8, raw);
-  }
-
-  f32x16 oacc[DT];
-#pragma unroll
-  for (int i = 0; i < DT; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
-  float m_run = -INFINITY;   // running row max, exp2 units
-  float l_run = 0.f;         // this lane's share of the row sum
+  for (int t = 0; t < KS; ++t)
+    qf[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rq, (qrow * D + 16 * t + 8 * half) * 2, 0, 0));
 
   const int kv_end = min(q0 + kBM, n);
   const int ntiles = (kv_end + kBN - 1) / kBN;
 
   u32x4 kreg[KCH];
   u32x4 vreg[4];
-  const int vpair = tid;                 // (key group, d chunk) handled by this thread
-  const int vkg = vpair % (kBN / 4), vdc = vpair / (kBN / 4);
+  const int vkg = tid % (kBN / 4), vdc = tid / (kBN / 4);   // (key group, d chunk) of this thread
 
   auto load_tile = [&](int tile) {
     const int key0 = tile * kBN;
@@ -106,18 +139,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(
     for (int i = 0; i < KCH; ++i) {
       const int ch = tid + kThreads * i;
       const int row = ch / (D / 8), col = ch % (D / 8);
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (key0 + row < n) z = *reinterpret_cast<const u32x4*>(k + kvbase + int64_t(key0 + row) * D + col * 8);
-      kreg[i] = z;
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((key0 + row) * D + col * 8) * 2, 0, 0);
     }
-    if (vpair < VPAIRS) {
+    if (tid < VPAIRS) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = key0 + 4 * vkg + r;
-        u32x4 z = {0u, 0u, 0u, 0u};
-        if (key < n) z = *reinterpret_cast<const u32x4*>(v + kvbase + int64_t(key) * D + vdc * 8);
-        vreg[r] = z;
-      }
+      for (int r = 0; r < 4; ++r)
+        vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((key0 + 4 * vkg + r) * D + vdc * 8) * 2, 0, 0);
     }
   };
   auto store_tile = [&](int buf) {
@@ -127,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(
       const int row = ch / (D / 8), col = ch % (D / 8);
       *reinterpret_cast<u32x4*>(&sm.k[buf][row][col * 8]) = kreg[i];
     }
-    if (vpair < VPAIRS) {
+    if (tid < VPAIRS) {
       // 4 keys x 8 d  ->  8 rows of V^T, 4 keys each
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -143,97 +170,128 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  const int wrow_min = q0 + 32 * wave;
-  const int wrow_max = wrow_min + 31;
   const int krow = perm32(l32);
+  const f32x16 zero = {};
 
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < ntiles) load_tile(tile + 1);
-    const int key0 = tile * kBN;
-    if (key0 <= wrow_max) {
-      f32x16 sacc[NSUB];
+  // S^T = K Q^T for the tile in `buf`: two independent accumulator chains.
+  auto qk = [&](int buf, f32x16 (&sacc)[NSUB]) {
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
 #pragma unroll
       for (int sb = 0; sb < NSUB; ++sb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[sb][e] = 0.f;
-#pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * sb + krow][16 * t + 8 * half]);
-          sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[sb], 0, 0, 0);
-        }
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * sb + krow][16 * t + 8 * half]);
+        sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? zero : sacc[sb], 0, 0, 0);
       }
-      // scale to exp2 units, causal mask, tile row max
-      const bool diag = key0 + kBN - 1 > wrow_min;
-      float mt = -INFINITY;
+  };
+  auto mask = [&](int key0, f32x16 (&sacc)[NSUB]) {
 #pragma unroll
-      for (int sb = 0; sb < NSUB; ++sb)
+    for (int sb = 0; sb < NSUB; ++sb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float x = sacc[sb][e] * c;
-          if (diag) {
-            const int key = key0 + 32 * sb + 16 * ((e >> 2) >> 1) + 8 * half + 4 * ((e >> 2) & 1) + (e & 3);
-            if (key > qrow) x = -INFINITY;
-          }
-          sacc[sb][e] = x;
-          mt = fmaxf(mt, x);
+      for (int e = 0; e < 16; ++e)
+        if (key0 + 32 * sb + acc_key(e, half) > qrow) sacc[sb][e] = -INFINITY;
+  };
+  auto tile_max = [&](const f32x16 (&sacc)[NSUB]) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, sacc[sb][e]);
+    return max_halves(m);
+  };
+
+  f32x16 oacc[DT];
+  float m_ref = 0.f;      // exp2 reference of this lane's row
+  float l_run = 0.f;      // this lane's share of the row sum
+
+  // P = exp2(S c - m_ref), row sums, then O^T += V^T P^T.
+  auto pv = [&](int buf, const f32x16 (&sacc)[NSUB]) {
+    const float mneg = -m_ref;
+    bf16x8 pb[NSUB * 2];
+    float ls = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        u32x4 pk;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[sb][8 * tt + 2 * e2], c, mneg));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[sb][8 * tt + 2 * e2 + 1], c, mneg));
+          ls += p0;
+          ls += p1;
+          pk[e2] = pack_bf16x2(p0, p1);
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);   // 0 on the first tile (m_run = -inf)
-      m_run = m_new;
-      float ls = 0.f;
-      bf16x8 pb[NSUB * 2];
+        pb[2 * sb + tt] = __builtin_bit_cast(bf16x8, pk);
+      }
+    l_run += ls;
 #pragma unroll
-      for (int sb = 0; sb < NSUB; ++sb)
+    for (int kk = 0; kk < NSUB * 2; ++kk)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          u32x4 pk;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const float p0 = exp2f(sacc[sb][8 * tt + 2 * e2] - m_new);
-            const float p1 = exp2f(sacc[sb][8 * tt + 2 * e2 + 1] - m_new);
-            ls += p0 + p1;
-            pk[e2] = pack_bf16x2(p0, p1);
-          }
-          pb[2 * sb + tt] = __builtin_bit_cast(bf16x8, pk);
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.vt[buf][32 * dt + l32][16 * kk + 8 * half]);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[dt], 0, 0, 0);
+      }
+  };
+
+  // attempt 0: reference = max of the first key tile; attempt 1 (rare): exact row max.
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    if (attempt == 1) {
+      float m = -INFINITY;
+      load_tile(0);
+      store_tile(0);
+      __syncthreads();
+      for (int tile = 0; tile < ntiles; ++tile) {
+        const int buf = tile & 1;
+        if (tile + 1 < ntiles) load_tile(tile + 1);
+        if (tile <= wdiag) {
+          f32x16 sacc[NSUB];
+          qk(buf, sacc);
+          if (tile == wdiag) mask(tile * kBN, sacc);
+          m = fmaxf(m, tile_max(sacc));
         }
-      l_run = l_run * alpha + ls;
-#pragma unroll
-      for (int i = 0; i < DT; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int kk = 0; kk < NSUB * 2; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.vt[buf][32 * dt + l32][16 * kk + 8 * half]);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[dt], 0, 0, 0);
-        }
+        if (tile + 1 < ntiles) store_tile(buf ^ 1);
+        __syncthreads();
+      }
+      m_ref = m * c;
     }
-    if (tile + 1 < ntiles) store_tile(buf ^ 1);
+#pragma unroll
+    for (int i = 0; i < DT; ++i) oacc[i] = zero;
+    l_run = 0.f;
+    load_tile(0);
+    store_tile(0);
     __syncthreads();
+    for (int tile = 0; tile < ntiles; ++tile) {
+      const int buf = tile & 1;
+      if (tile + 1 < ntiles) load_tile(tile + 1);
+      if (tile < wdiag && tile > 0) {
+        f32x16 sacc[NSUB];              // hot path: no mask, no reductions
+        qk(buf, sacc);
+        pv(buf, sacc);
+      } else if (tile <= wdiag) {
+        f32x16 sacc[NSUB];
+        qk(buf, sacc);
+        if (tile == wdiag) mask(tile * kBN, sacc);
+        if (tile == 0 && attempt == 0) m_ref = tile_max(sacc) * c;
+        pv(buf, sacc);
+      }
+      if (tile + 1 < ntiles) store_tile(buf ^ 1);
+      __syncthreads();
+    }
+    const bool bad = !(sum_halves(l_run) <= kSumLimit);
+    if (!__syncthreads_or(bad)) break;
   }
 
-  // epilogue: O = O^T / l, lane holds d = 32dt + 8g + 4*half + {0..3} of its row
-  const float l = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l;
-  if (qrow < n) {
-    uint16_t* orow = o + qbase + int64_t(qrow) * D;
+  // epilogue: O = O^T / l; lane holds d = 32dt + 8g + 4*half + {0..3} of its row.
+  const float inv = 1.0f / sum_halves(l_run);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 pk;
-        pk.x = pack_bf16x2(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
-        pk.y = pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * g + 4 * half) = pk;
-      }
-  }
+    for (int g = 0; g < 4; ++g) {
+      u32x2 pk;
+      pk.x = pack_bf16x2(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
+      pk.y = pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+      __builtin_amdgcn_raw_buffer_store_b64(pk, ro, (qrow * D + 32 * dt + 8 * g + 4 * half) * 2, 0, 0);
+    }
 }
 
 // ---------------------------------------------------------------- f32 VALU

@@ -44,7 +44,7 @@ tsa_status check_problem(const tsa_problem* p, tsa::Shape* out) {
     return fail(TSA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", p->Hq, p->Hkv);
   if (p->w > p->L) return fail(TSA_ERR_INVALID_ARG, "w=%d exceeds L=%d", p->w, p->L);
   if (p->Hq > tsa::kMaxHq) return fail(TSA_ERR_INVALID_ARG, "Hq=%d exceeds %d", p->Hq, tsa::kMaxHq);
-  if (int64_t(p->L) > tsa::kMaxL) return fail(TSA_ERR_INVALID_ARG, "L=%d exceeds 2^28", p->L);
+  if (int64_t(p->L) > tsa::kMaxL) return fail(TSA_ERR_INVALID_ARG, "L=%d exceeds 2^22", p->L);
   if (std::isnan(p->tau) || !(p->tau >= 0.0f) || !(p->tau < 1.0f))
     return fail(TSA_ERR_INVALID_ARG, "tau=%g is outside [0, 1)", double(p->tau));
   if (p->dtype != TSA_F32 && p->dtype != TSA_BF16)
