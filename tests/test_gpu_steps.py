@@ -228,3 +228,32 @@ def test_attention_deterministic_and_tau0_equals_dense():
     assert int(budget[0]) == 1000
     assert torch.equal(dense.view(torch.int16), dense2.view(torch.int16))
     assert torch.equal(o.view(torch.int16), dense.view(torch.int16))
+
+
+def _bf16_round(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("late_key", [700, 130])
+def test_attention_recompute_on_large_late_logit(late_key):
+    """A key well past the first tile whose logit exceeds every first-tile logit
+    by far more than 2^64 in weight forces the exact-max recompute; the result
+    must still match the oracle (and rows before that key are unaffected)."""
+    say(f"case attention large late logit at key {late_key}")
+    B, H, L, d = 1, 2, 900, 128
+    rng = np.random.default_rng(77)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = rng.standard_normal((B, H, L, d))
+    k = rng.standard_normal((B, H, L, d))
+    v = rng.standard_normal((B, H, L, d))
+    q[:, :, late_key:] += 10.0 * u
+    k[:, :, late_key] = 80.0 * u
+    q, k, v = _bf16_round(q), _bf16_round(k), _bf16_round(v)
+    prob = T.Problem(B, H, H, L, d, 1, 0.05, "bf16")
+    o = to_np(T.tsa_attention(prob, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), None, 1))
+    for h in range(H):
+        ref = O.causal_attention(q[0, h], k[0, h], v[0, h])
+        assert_outputs_close(o[0, h], ref, "bf16", what=f" h={h}")
+        # rows after the key are dominated by it
+        assert np.allclose(ref[late_key + 1:], v[0, h, late_key], atol=1e-3)

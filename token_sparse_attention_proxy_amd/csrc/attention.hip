@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   auto pv = [&](int buf, const f32x16 (&sacc)[NSUB]) {
     const float mneg = -m_ref;
     bf16x8 pb[NSUB * 2];
-    float ls = 0.f;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};      // independent partial sums
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb)
 #pragma unroll
@@ -217,13 +217,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
         for (int e2 = 0; e2 < 4; ++e2) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[sb][8 * tt + 2 * e2], c, mneg));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[sb][8 * tt + 2 * e2 + 1], c, mneg));
-          ls += p0;
-          ls += p1;
+          ls[(2 * e2) & 3] += p0;
+          ls[(2 * e2 + 1) & 3] += p1;
           pk[e2] = pack_bf16x2(p0, p1);
         }
         pb[2 * sb + tt] = __builtin_bit_cast(bf16x8, pk);
       }
-    l_run += ls;
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
     for (int kk = 0; kk < NSUB * 2; ++kk)
 #pragma unroll

@@ -23,9 +23,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   __bf16 h = static_cast<__bf16>(f);
   return __builtin_bit_cast(uint16_t, h);
 }
-// Two floats -> packed bf16 pair (lo = a, hi = b), round to nearest even.
+// Two floats -> packed bf16 pair (lo = a, hi = b), round to nearest even
+// (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return uint32_t(f32_to_bf16_bits(a)) | (uint32_t(f32_to_bf16_bits(b)) << 16);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Element access for the two storage types.
