@@ -90,6 +90,7 @@ BAD_PROBLEMS = [
     (dict(d=96), _lib.TSA_ERR_UNSUPPORTED),
     (dict(d=256), _lib.TSA_ERR_UNSUPPORTED),
     (dict(dtype=7), _lib.TSA_ERR_UNSUPPORTED),
+    (dict(Hq=64, Hkv=1, w=1000), _lib.TSA_ERR_UNSUPPORTED),
 ]
 
 

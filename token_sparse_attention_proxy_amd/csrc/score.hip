@@ -6,12 +6,23 @@
 // An exact softmax needs every row's max and normaliser before any column
 // sum can be formed, so the work is two streaming passes over K plus a small
 // merge; no L x w buffer is ever held:
-//   pass 1  per (key chunk, head): per-row (max, sum of exp) over the chunk
+//   pass 1  per (key chunk, KV head): per-row (max, sum of exp) over the chunk
 //   merge   per proxy row: global max and 1/Z, chunk partials combined in fp64
-//   pass 2  per (key chunk, head): s_j = (1/w) sum_r exp2(x_rj - M_r) / Z_r
-// Logits are kept in exp2 units: x = <q, k> * log2(e)/sqrt(d).  Both passes
-// evaluate x with the same code, so pass 2 sees exactly the values pass 1
-// reduced.  All reductions run in a fixed order: the result is deterministic.
+//   pass 2  per (key chunk, KV head): s_j = (1/w) sum_r exp2(x_rj - M_r) / Z_r
+// Logits are kept in exp2 units: x = <q, k> * log2(e)/sqrt(d).  Every
+// reduction runs in a fixed order, so the result is deterministic.
+//
+// bf16 path (gfx950 MFMA): one workgroup per (128-key chunk, KV head) stages
+// the chunk of K in LDS once and serves all G*w proxy rows of the group's
+// query heads, as 32-row tiles (a head's rows are padded to whole tiles).
+// Pass 1 computes S^T = K Q^T (v_mfma_f32_32x32x16_bf16) so each lane owns a
+// proxy row and keeps an online (max, sum); pass 2 computes S = Q K^T so each
+// lane owns a key column and sums the 16 rows it holds, then the two lane
+// halves, then the row tiles of the head (through LDS, in tile order).  The Q
+// fragments and the LDS K reads are identical in the two orientations.
+// f32 path: plain fp32 VALU kernels (one key per thread).
+#include <type_traits>
+
 #include "tsa_device.h"
 #include "tsa_internal.h"
 
@@ -155,6 +166,177 @@ __global__ __launch_bounds__(kThreads) void score_pass2(const T* __restrict__ q,
   if (j < L) s[int64_t(bh) * L + j] = acc / float(w);
 }
 
+// ---------------------------------------------------------------- bf16 MFMA
+constexpr int kMThreads = 256;          // 4 waves
+constexpr int kMPad = 8;                // bf16 padding per K row in LDS
+
+// Stage K rows [j0, j0 + kScoreChunk) of one KV head in LDS (rows past L read as 0).
+template <int D>
+__device__ __forceinline__ void stage_k_chunk(const uint16_t* __restrict__ kg, int L, int j0,
+                                              uint16_t (*ks)[D + kMPad]) {
+  constexpr int CPR = D / 8;
+  for (int ch = threadIdx.x; ch < kScoreChunk * CPR; ch += kMThreads) {
+    const int row = ch / CPR, col = ch % CPR;
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (j0 + row < L) z = *reinterpret_cast<const u32x4*>(kg + int64_t(j0 + row) * D + col * 8);
+    *reinterpret_cast<u32x4*>(&ks[row][col * 8]) = z;
+  }
+}
+
+// Q fragments of one 32-row proxy tile: lane holds q[row l%32][16t + 8*(l/32) .. +8];
+// rows past w are zero.
+template <int D>
+__device__ __forceinline__ void load_q_tile(const uint16_t* __restrict__ qh, int L, int w, int r0,
+                                            bf16x8 (&qf)[D / 16]) {
+  const int lane = threadIdx.x & 63;
+  const int r = r0 + (lane & 31), half = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (r < w) z = *reinterpret_cast<const u32x4*>(qh + int64_t(L - w + r) * D + 16 * t + 8 * half);
+    qf[t] = __builtin_bit_cast(bf16x8, z);
+  }
+}
+
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float xhalf_other(float x) {
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const int lane = threadIdx.x & 63;
+  return __uint_as_float(lane < 32 ? sw[1] : sw[0]);
+}
+
+// Pass 1: per proxy row, (max, sum of exp2(x - max)) over the chunk's visible keys.
+template <int D>
+__global__ __launch_bounds__(kMThreads) void score_mfma_rowstats(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, float2* __restrict__ part,
+    int Hq, int Hkv, int L, int w, int n_chunk, float c) {
+  constexpr int KS = D / 16;
+  __shared__ uint16_t ks[kScoreChunk][D + kMPad];
+  const int chunk = blockIdx.x, bg = blockIdx.y;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int G = Hq / Hkv, RT = (w + 31) / 32;
+  const int j0 = chunk * kScoreChunk;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l32 = lane & 31, half = lane >> 5;
+  stage_k_chunk<D>(k + (int64_t(b) * Hkv + g) * L * D, L, j0, ks);
+  __syncthreads();
+  // keys of this chunk that some proxy row cannot see: masking needed
+  const bool edge = j0 + kScoreChunk - 1 > L - w;
+  const f32x16 zero = {};
+  for (int unit = wave; unit < G * RT; unit += kMThreads / 64) {
+    const int h = g * G + unit / RT, r0 = 32 * (unit % RT);
+    const int bh = b * Hq + h;
+    bf16x8 qf[KS];
+    load_q_tile<D>(q + int64_t(bh) * L * D, L, w, r0, qf);
+    const int r = r0 + l32;                 // this lane's proxy row
+    const int pos = L - w + r;              // its sequence position
+    float m = -INFINITY, z = 0.f;
+    for (int kt = 0; kt < kScoreChunk / 32; ++kt) {
+      f32x16 acc;
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ks[32 * kt + l32][16 * t + 8 * half]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? zero : acc, 0, 0, 0);
+      }
+      float x[16];
+      float tm = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = j0 + 32 * kt + 8 * (e >> 2) + 4 * half + (e & 3);
+        x[e] = acc[e] * c;
+        if (edge && (key > pos || r >= w)) x[e] = -INFINITY;
+        tm = fmaxf(tm, x[e]);
+      }
+      const float mn = fmaxf(m, tm);
+      if (mn == -INFINITY) continue;        // nothing visible yet for this lane
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(x[e] - mn);
+      z = z * __builtin_amdgcn_exp2f(m - mn) + sum;
+      m = mn;
+    }
+    // combine the two lane halves, which saw different keys of the same row
+    const float mo = xhalf_other(m), zo = xhalf_other(z);
+    const float M = fmaxf(m, mo);
+    float Z = 0.f;
+    if (M != -INFINITY) {
+      if (m != -INFINITY) Z += z * __builtin_amdgcn_exp2f(m - M);
+      if (mo != -INFINITY) Z += zo * __builtin_amdgcn_exp2f(mo - M);
+    }
+    if (half == 0 && r < w) part[((int64_t(bh) * w) + r) * n_chunk + chunk] = make_float2(M, Z);
+  }
+}
+
+// Pass 2: column sums of the normalised proxy rows, per head, divided by w.
+template <int D>
+__global__ __launch_bounds__(kMThreads) void score_mfma_colsum(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const float2* __restrict__ rowstat, float* __restrict__ s, int Hq, int Hkv, int L, int w,
+    float c) {
+  constexpr int KS = D / 16;
+  extern __shared__ float colsum[];       // [G*RT][kScoreChunk]
+  __shared__ uint16_t ks[kScoreChunk][D + kMPad];
+  const int chunk = blockIdx.x, bg = blockIdx.y;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int G = Hq / Hkv, RT = (w + 31) / 32;
+  const int j0 = chunk * kScoreChunk;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l32 = lane & 31, half = lane >> 5;
+  stage_k_chunk<D>(k + (int64_t(b) * Hkv + g) * L * D, L, j0, ks);
+  __syncthreads();
+  const bool edge = j0 + kScoreChunk - 1 > L - w;
+  const f32x16 zero = {};
+  for (int unit = wave; unit < G * RT; unit += kMThreads / 64) {
+    const int h = g * G + unit / RT, r0 = 32 * (unit % RT);
+    const int bh = b * Hq + h;
+    bf16x8 qf[KS];
+    load_q_tile<D>(q + int64_t(bh) * L * D, L, w, r0, qf);
+    // statistics of the 16 rows this lane holds in the accumulator
+    float mrow[16], izrow[16];
+    int prow[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rr = r0 + 8 * (v >> 2) + 4 * half + (v & 3);
+      float2 st = make_float2(0.f, 0.f);
+      if (rr < w) st = rowstat[int64_t(bh) * w + rr];
+      mrow[v] = st.x;
+      izrow[v] = st.y;                    // 0 for padding rows: they add nothing
+      prow[v] = L - w + rr;
+    }
+    for (int kt = 0; kt < kScoreChunk / 32; ++kt) {
+      f32x16 acc;
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&ks[32 * kt + l32][16 * t + 8 * half]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t], bk, t == 0 ? zero : acc, 0, 0, 0);
+      }
+      const int key = j0 + 32 * kt + l32;
+      float cs = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float p = __builtin_amdgcn_exp2f(fmaf(acc[v], c, -mrow[v])) * izrow[v];
+        if (edge && key > prow[v]) p = 0.f;
+        cs += p;
+      }
+      cs += xhalf_other(cs);
+      if (half == 0) colsum[unit * kScoreChunk + 32 * kt + l32] = cs;
+    }
+  }
+  __syncthreads();
+  // s = (sum over the head's row tiles, in tile order) / w
+  for (int i = threadIdx.x; i < G * kScoreChunk; i += kMThreads) {
+    const int hl = i / kScoreChunk, kk = i % kScoreChunk;
+    const int j = j0 + kk;
+    if (j >= L) continue;
+    float acc = 0.f;
+    for (int rt = 0; rt < RT; ++rt) acc += colsum[(hl * RT + rt) * kScoreChunk + kk];
+    s[(int64_t(b) * Hq + g * G + hl) * L + j] = acc / float(w);
+  }
+}
+
 template <typename T, int D>
 hipError_t run(const Shape& sh, const void* q, const void* k, float* scores, char* ws,
                hipStream_t st) {
@@ -163,13 +345,26 @@ hipError_t run(const Shape& sh, const void* q, const void* k, float* scores, cha
   float2* rowstat = reinterpret_cast<float2*>(ws + lay.rowstat);
   const float c = kLog2e / sqrtf(float(D));
   const int nc = sh.n_chunk();
-  dim3 grid(nc, sh.B * sh.Hq);
-  score_pass1<T, D><<<grid, kThreads, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
-                                               part, sh.Hq, sh.Hkv, sh.L, sh.w, nc, c);
   const int64_t rows = int64_t(sh.B) * sh.Hq * sh.w;
-  score_merge<<<unsigned((rows + 255) / 256), 256, 0, st>>>(part, rowstat, rows, nc);
-  score_pass2<T, D><<<grid, kThreads, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
-                                               rowstat, scores, sh.Hq, sh.Hkv, sh.L, sh.w, c);
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    const dim3 grid(nc, sh.B * sh.Hkv);
+    const int units = sh.G() * ((sh.w + 31) / 32);
+    const size_t colsum_bytes = sizeof(float) * size_t(units) * kScoreChunk;
+    score_mfma_rowstats<D><<<grid, kMThreads, 0, st>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), part, sh.Hq, sh.Hkv,
+        sh.L, sh.w, nc, c);
+    score_merge<<<unsigned((rows + 255) / 256), 256, 0, st>>>(part, rowstat, rows, nc);
+    score_mfma_colsum<D><<<grid, kMThreads, colsum_bytes, st>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), rowstat, scores, sh.Hq,
+        sh.Hkv, sh.L, sh.w, c);
+  } else {
+    const dim3 grid(nc, sh.B * sh.Hq);
+    score_pass1<T, D><<<grid, kThreads, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
+                                                 part, sh.Hq, sh.Hkv, sh.L, sh.w, nc, c);
+    score_merge<<<unsigned((rows + 255) / 256), 256, 0, st>>>(part, rowstat, rows, nc);
+    score_pass2<T, D><<<grid, kThreads, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
+                                                 rowstat, scores, sh.Hq, sh.Hkv, sh.L, sh.w, c);
+  }
   return hipGetLastError();
 }
 

@@ -51,6 +51,10 @@ tsa_status check_problem(const tsa_problem* p, tsa::Shape* out) {
     return fail(TSA_ERR_UNSUPPORTED, "dtype %d is not supported (TSA_F32=0, TSA_BF16=1)", p->dtype);
   if (p->d != 64 && p->d != 128)
     return fail(TSA_ERR_UNSUPPORTED, "head dim d=%d is not supported (64 or 128)", p->d);
+  if (p->dtype == TSA_BF16 && (p->Hq / p->Hkv) * ((p->w + 31) / 32) > tsa::kMaxScoreTiles)
+    return fail(TSA_ERR_UNSUPPORTED,
+                "(Hq/Hkv) * ceil(w/32) = %d proxy-row tiles per KV head exceeds %d",
+                (p->Hq / p->Hkv) * ((p->w + 31) / 32), tsa::kMaxScoreTiles);
   *out = tsa::Shape{p->B, p->Hq, p->Hkv, p->L, p->d, p->w, p->tau, p->dtype};
   return TSA_OK;
 }
