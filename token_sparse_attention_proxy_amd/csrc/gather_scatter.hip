@@ -16,34 +16,40 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = 64;
 
-// VPR: 16-byte vectors per row (row bytes / 16).
+// VPR: 16-byte vectors per row (row bytes / 16).  One block copies compact
+// rows [i0, i0 + kRowsPerBlock) for all G query heads of one KV group, head
+// after head: the heads of a group select nearly the same tokens, so their
+// K/V source rows are read from HBM once and then hit in cache.
 template <int VPR>
 __global__ __launch_bounds__(kThreads) void gather_rows(
     const u32x4* __restrict__ q, const u32x4* __restrict__ k, const u32x4* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ budget, u32x4* __restrict__ qc,
     u32x4* __restrict__ kc, u32x4* __restrict__ vc, int Hq, int Hkv, int L) {
   constexpr int kRowsPerPass = kThreads / VPR;
-  const int bh = blockIdx.y;
-  const int b = bh / Hq, h = bh % Hq;
-  const int g = h / (Hq / Hkv);
+  const int bg = blockIdx.y;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int G = Hq / Hkv;
   const int n = min(max(budget[b], 0), L);
   const int i0 = blockIdx.x * kRowsPerBlock;
   if (i0 >= n) return;
   const int sub = threadIdx.x / VPR, vec = threadIdx.x % VPR;
-  const int64_t hrow = int64_t(bh) * L;                   // first row of (b,h)
   const int64_t grow = (int64_t(b) * Hkv + g) * L;        // first row of (b,g)
-  for (int i = i0 + sub; i < min(i0 + kRowsPerBlock, n); i += kRowsPerPass) {
-    const int src = idx[hrow + i];
-    const int64_t dst = (hrow + i) * VPR + vec;
-    if (src >= 0 && src < L) {
-      qc[dst] = q[(hrow + src) * VPR + vec];
-      kc[dst] = k[(grow + src) * VPR + vec];
-      vc[dst] = v[(grow + src) * VPR + vec];
-    } else {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      qc[dst] = z;
-      kc[dst] = z;
-      vc[dst] = z;
+  const int i1 = min(i0 + kRowsPerBlock, n);
+  for (int hl = 0; hl < G; ++hl) {
+    const int64_t hrow = (int64_t(b) * Hq + g * G + hl) * L;   // first row of (b,h)
+    for (int i = i0 + sub; i < i1; i += kRowsPerPass) {
+      const int src = idx[hrow + i];
+      const int64_t dst = (hrow + i) * VPR + vec;
+      if (src >= 0 && src < L) {
+        qc[dst] = q[(hrow + src) * VPR + vec];
+        kc[dst] = k[(grow + src) * VPR + vec];
+        vc[dst] = v[(grow + src) * VPR + vec];
+      } else {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        qc[dst] = z;
+        kc[dst] = z;
+        vc[dst] = z;
+      }
     }
   }
 }
@@ -69,7 +75,7 @@ template <int VPR>
 hipError_t gather_vpr(const Shape& sh, const void* q, const void* k, const void* v,
                       const int32_t* idx, const int32_t* budget, void* qc, void* kc, void* vc,
                       hipStream_t st) {
-  dim3 grid((sh.L + kRowsPerBlock - 1) / kRowsPerBlock, sh.B * sh.Hq);
+  dim3 grid((sh.L + kRowsPerBlock - 1) / kRowsPerBlock, sh.B * sh.Hkv);
   gather_rows<VPR><<<grid, kThreads, 0, st>>>(
       static_cast<const u32x4*>(q), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
       idx, budget, static_cast<u32x4*>(qc), static_cast<u32x4*>(kc), static_cast<u32x4*>(vc),

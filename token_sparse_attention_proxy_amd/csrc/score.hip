@@ -113,18 +113,27 @@ __global__ __launch_bounds__(kThreads) void score_pass1(const T* __restrict__ q,
   }
 }
 
-// One thread per proxy row: combine chunk partials (sums in fp64).
-__global__ void score_merge(const float2* __restrict__ part, float2* __restrict__ rowstat,
-                            int64_t rows, int n_chunk) {
-  const int64_t r = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (r >= rows) return;
+// One wave per proxy row: combine the chunk partials.  Lane i takes chunks
+// i, i+64, ...; the row max is a wave max, the sum is accumulated in fp64 per
+// lane and then reduced over the lanes in a fixed butterfly order, so the
+// result is deterministic.
+constexpr int kMergeWaves = 4;
+__global__ __launch_bounds__(64 * kMergeWaves) void score_merge(const float2* __restrict__ part,
+                                                                float2* __restrict__ rowstat,
+                                                                int64_t rows, int n_chunk) {
+  const int64_t r = int64_t(blockIdx.x) * kMergeWaves + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;                   // whole wave exits together
   const float2* p = part + r * n_chunk;
   float m = -INFINITY;
-  for (int i = 0; i < n_chunk; ++i) m = fmaxf(m, p[i].x);
+  for (int i = lane; i < n_chunk; i += 64) m = fmaxf(m, p[i].x);
+  m = wave_max(m);
   double z = 0.0;
-  for (int i = 0; i < n_chunk; ++i)
+  for (int i = lane; i < n_chunk; i += 64)
     if (p[i].x != -INFINITY) z += double(p[i].y) * exp2(double(p[i].x) - double(m));
-  rowstat[r] = make_float2(m, float(1.0 / z));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o, 64);
+  if (lane == 0) rowstat[r] = make_float2(m, float(1.0 / z));
 }
 
 template <typename T, int D>
@@ -353,7 +362,8 @@ hipError_t run(const Shape& sh, const void* q, const void* k, float* scores, cha
     score_mfma_rowstats<D><<<grid, kMThreads, 0, st>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), part, sh.Hq, sh.Hkv,
         sh.L, sh.w, nc, c);
-    score_merge<<<unsigned((rows + 255) / 256), 256, 0, st>>>(part, rowstat, rows, nc);
+    score_merge<<<unsigned((rows + kMergeWaves - 1) / kMergeWaves), 64 * kMergeWaves, 0, st>>>(
+        part, rowstat, rows, nc);
     score_mfma_colsum<D><<<grid, kMThreads, colsum_bytes, st>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), rowstat, scores, sh.Hq,
         sh.Hkv, sh.L, sh.w, c);
@@ -361,7 +371,8 @@ hipError_t run(const Shape& sh, const void* q, const void* k, float* scores, cha
     const dim3 grid(nc, sh.B * sh.Hq);
     score_pass1<T, D><<<grid, kThreads, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
                                                  part, sh.Hq, sh.Hkv, sh.L, sh.w, nc, c);
-    score_merge<<<unsigned((rows + 255) / 256), 256, 0, st>>>(part, rowstat, rows, nc);
+    score_merge<<<unsigned((rows + kMergeWaves - 1) / kMergeWaves), 64 * kMergeWaves, 0, st>>>(
+        part, rowstat, rows, nc);
     score_pass2<T, D><<<grid, kThreads, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
                                                  rowstat, scores, sh.Hq, sh.Hkv, sh.L, sh.w, c);
   }

@@ -1,0 +1,132 @@
+"""HBM traffic of the attention kernel from rocprofv3 counters.
+
+Two sub-commands, meant to run under rocprofv3 and after it:
+
+  python -m token_sparse_attention_proxy_amd.profiling run --workload NAME
+      Runs, in one process: a plain device-to-device copy of COPY_BYTES
+      (calibration), then the attention kernel on the compact shape of the
+      workload with its measured budget (inputs are random bf16 made on the
+      GPU; traffic depends on shapes and the budget, not on values).  Run it
+      twice under ``rocprofv3 --pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``.
+
+  python -m token_sparse_attention_proxy_amd.profiling summarize \\
+        --fetch DIR --write DIR --workload NAME --budget K [--out profiles/traffic.json]
+      Reads the two counter CSVs, scales each counter by what it reads for
+      the copy (bytes moved / counter bytes), and records the attention
+      kernel's HBM bytes per launch, keyed by the kernel source hash, so that
+      bench.py reports them only while the kernel is unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ATTN_SRC = os.path.join(ROOT, "token_sparse_attention_proxy_amd", "csrc", "attention.hip")
+COPY_BYTES = 1 << 30
+
+
+def source_sha(path: str = ATTN_SRC) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def cmd_run(args):
+    import torch
+    sys.path.insert(0, ROOT)
+    from token_sparse_attention_proxy_amd import inputs
+    from token_sparse_attention_proxy_amd import tsa as T
+
+    wl = inputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)                       # calibration: COPY_BYTES read, COPY_BYTES written
+    torch.cuda.synchronize()
+    del src, dst
+    g = torch.Generator(device=dev).manual_seed(0)
+    shape = (wl.B, wl.Hq, wl.L, wl.d)
+    q, k, v = (torch.randn(shape, device=dev, generator=g).to(torch.bfloat16) for _ in range(3))
+    bud = torch.full((wl.B,), args.budget, dtype=torch.int32, device=dev)
+    prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, wl.taus[0], wl.dtype)
+    o = torch.empty_like(q)
+    T.tsa_attention(prob, q, k, v, bud, 1, o)
+    torch.cuda.synchronize()
+    print(f"ran copy of {COPY_BYTES} B and attention on {shape} with budget {args.budget}")
+
+
+def _read(dirpath: str, counter: str):
+    rows = []
+    for f in glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                rows.append((r.get("Kernel_Name", ""), float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {dirpath}")
+    return rows
+
+
+def _pick(rows, needle):
+    vals = [v for name, v in rows if needle in name]
+    if not vals:
+        raise SystemExit(f"no kernel matching {needle!r}")
+    return vals
+
+
+def cmd_summarize(args):
+    fetch = _read(args.fetch, "FETCH_SIZE")
+    write = _read(args.write, "WRITE_SIZE")
+    # the copy is the largest-FETCH non-attention kernel
+    copy_f = max(v for n, v in fetch if "attn_fwd" not in n) * 1024.0
+    copy_w = max(v for n, v in write if "attn_fwd" not in n) * 1024.0
+    f_scale = COPY_BYTES / copy_f
+    w_scale = COPY_BYTES / copy_w
+    af = _pick(fetch, "attn_fwd")
+    aw = _pick(write, "attn_fwd")
+    fetch_b = sum(af) / len(af) * 1024.0 * f_scale
+    write_b = sum(aw) / len(aw) * 1024.0 * w_scale
+    entry = {
+        "source_sha": source_sha(),
+        "budget": args.budget,
+        "fetch_bytes_per_launch": fetch_b,
+        "write_bytes_per_launch": write_b,
+        "bytes_per_launch": fetch_b + write_b,
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "copy_bytes": COPY_BYTES,
+    }
+    tab = {}
+    if os.path.exists(args.out):
+        with open(args.out) as f:
+            tab = json.load(f)
+    tab.setdefault("attn_fwd_bf16", {})[args.workload] = entry
+    with open(args.out, "w") as f:
+        json.dump(tab, f, indent=1, sort_keys=True)
+    print(json.dumps(entry, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--workload", default="llama8b_bf16_L128k")
+    r.add_argument("--budget", type=int, default=123997)
+    r.set_defaults(fn=cmd_run)
+    s = sub.add_parser("summarize")
+    s.add_argument("--fetch", required=True)
+    s.add_argument("--write", required=True)
+    s.add_argument("--workload", default="llama8b_bf16_L128k")
+    s.add_argument("--budget", type=int, default=123997)
+    s.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    s.set_defaults(fn=cmd_summarize)
+    args = ap.parse_args()
+    args.fn(args)
+
+
+if __name__ == "__main__":
+    main()
