@@ -83,7 +83,7 @@ def cpu_baseline(wl, q, k, v, tau, K_gpu: int):
     qc, kc, vc = O.gather(q[:1, :1], k[:1, :1], v[:1, :1], idx, budget[:1])
     t_gather = (time.perf_counter() - t0) * B * Hq
     # attention on the last rows of the compact sequence (the most expensive ones)
-    n_rows = min(K, 6144 if L >= 65536 else 8192)
+    n_rows = min(K, 24576 if L >= 65536 else 8192)
     rows = np.arange(K - n_rows, K)
     t0 = time.perf_counter()
     oc_rows = O.causal_attention(qc[0, 0, :K], kc[0, 0, :K], vc[0, 0, :K], rows=rows)
