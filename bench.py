@@ -1,16 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the Token Sparse Attention prefill op on one MI355X.
 
-One step = one tsa_forward over one batch (score -> budget -> select ->
-gather -> causal attention -> scatter) on seeded synthetic Q, K, V that are
-already resident in HBM.  Printed as one JSON line, with:
+One step = one pass of the whole op over one batch of seeded synthetic Q, K,
+V already resident in HBM.  Two paths compute it, bit for bit alike:
+  fused: tsa_forward_fused = score -> budget -> select -> zero the
+      unselected output rows -> attention reading Q, K, V through the index
+      set and writing O rows to their sequence positions;
+  steps (default): tsa_forward = score -> budget -> select -> gather -> attention on
+      the compact tensors -> scatter.
+The chosen path is timed for K steps; the other is timed too and reported.
+Printed as one JSON line, with:
   * the dense causal attention baseline (same attention kernel, GQA head map,
-    no gather / scatter) and the speedup against it;
-  * a per-step breakdown timed with HIP events on the launch stream, and the
-    roofline of the dominant kernel (the attention) from that timed region;
+    no selection) and the speedup against it;
+  * a per-kernel breakdown of both paths timed with HIP events on the launch
+    stream, and the roofline of the dominant kernel (the attention of the
+    timed path) from those launches;
   * the fp64 CPU oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--path fused|steps]
 """
 from __future__ import annotations
 
@@ -118,6 +126,7 @@ def main():
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--path", choices=["fused", "steps"], default="steps")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -147,52 +156,77 @@ def main():
     idx = torch.empty((wl.B, wl.Hq, wl.L), dtype=torch.int32, device=dev)
     ws = torch.empty(T.forward_workspace_bytes(prob), dtype=torch.uint8, device=dev)
     st = torch.cuda.current_stream(dev)
+    paths = {"fused": lambda: T.tsa_forward_fused(prob, qd, kd, vd, o, budget, idx, ws),
+             "steps": lambda: T.tsa_forward(prob, qd, kd, vd, o, budget, idx, ws)}
+    other = "steps" if args.path == "fused" else "fused"
 
-    # ---- headline: K timed steps of the fused forward
-    log(f"[bench] warmup {args.warmup}")
+    # ---- headline: K timed steps of the chosen path
+    log(f"[bench] warmup {args.warmup} ({args.path})")
     for _ in range(args.warmup):
-        T.tsa_forward(prob, qd, kd, vd, o, budget, idx, ws)
+        paths[args.path]()
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        T.tsa_forward(prob, qd, kd, vd, o, budget, idx, ws)
+        paths[args.path]()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     bud = budget.cpu().numpy()
-    log(f"[bench] tsa_forward {ms_step:.3f} ms/step, budget {bud} K/L {bud / wl.L}")
+    log(f"[bench] {args.path} {ms_step:.3f} ms/step, budget {bud} K/L {bud / wl.L}")
 
-    # ---- per-step breakdown: the same kernels called one by one, HIP events between them
+    # ---- the other path, for comparison (same results)
+    oreps = max(2, min(args.steps, 5))
+    paths[other]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(oreps):
+        paths[other]()
+    torch.cuda.synchronize()
+    other_ms = (time.perf_counter() - t0) * 1e3 / oreps
+    log(f"[bench] {other} {other_ms:.3f} ms/step")
+
+    # ---- per-kernel breakdown: the kernels called one by one, HIP events between them
     heads = wl.B * wl.Hq
     step_ws = torch.empty(T.workspace_bytes(prob), dtype=torch.uint8, device=dev)
     s = torch.empty((wl.B, wl.Hq, wl.L), dtype=torch.float32, device=dev)
     rank = torch.empty_like(idx)
     qc, kc, vc, oc = (torch.empty(shape, dtype=tdt, device=dev) for _ in range(4))
-    names = ["score", "budget", "select", "gather", "attention", "scatter"]
+    calls = {
+        "score": lambda: T.tsa_score(prob, qd, kd, s, step_ws),
+        "budget": lambda: T.tsa_budget(prob, s, budget, step_ws),
+        "select": lambda: T.tsa_select(prob, s, budget, idx, rank, step_ws),
+        "gather": lambda: T.tsa_gather(prob, qd, kd, vd, idx, budget, qc, kc, vc),
+        "attention": lambda: T.tsa_attention(prob, qc, kc, vc, budget, 1, oc),
+        "scatter": lambda: T.tsa_scatter(prob, oc, rank, o),
+        "attention_indexed": lambda: T.tsa_attention_indexed(prob, qd, kd, vd, idx, budget, o),
+    }
+    names = list(calls)
     acc = {n: 0.0 for n in names}
     reps = max(3, min(args.steps, 10))
     for rep in range(reps + 1):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
         ev[0].record(st)
-        T.tsa_score(prob, qd, kd, s, step_ws)
-        ev[1].record(st)
-        T.tsa_budget(prob, s, budget, step_ws)
-        ev[2].record(st)
-        T.tsa_select(prob, s, budget, idx, rank, step_ws)
-        ev[3].record(st)
-        T.tsa_gather(prob, qd, kd, vd, idx, budget, qc, kc, vc)
-        ev[4].record(st)
-        T.tsa_attention(prob, qc, kc, vc, budget, 1, oc)
-        ev[5].record(st)
-        T.tsa_scatter(prob, oc, rank, o)
-        ev[6].record(st)
+        for i, n in enumerate(names):
+            calls[n]()
+            ev[i + 1].record(st)
         torch.cuda.synchronize()
         if rep > 0:       # first pass is a warm-up
             for i, n in enumerate(names):
                 acc[n] += ev[i].elapsed_time(ev[i + 1])
     steps_ms = {n: acc[n] / reps for n in names}
-    log("[bench] steps ms: " + ", ".join(f"{n} {steps_ms[n]:.3f}" for n in names))
+    # the fused path's zero fill is internal to tsa_forward_fused: its time is
+    # the fused step (event-timed) minus the four kernels timed above
+    ef0, ef1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ef0.record(st)
+    for _ in range(reps):
+        paths["fused"]()
+    ef1.record(st)
+    torch.cuda.synchronize()
+    fused_ev_ms = ef0.elapsed_time(ef1) / reps
+    steps_ms["zero_fill"] = max(0.0, fused_ev_ms - sum(steps_ms[n] for n in
+                                                       ("score", "budget", "select", "attention_indexed")))
+    log("[bench] kernels ms: " + ", ".join(f"{n} {steps_ms[n]:.3f}" for n in steps_ms))
 
     # ---- dense causal attention baseline (same kernel, GQA head map)
     dense_ms = None
@@ -212,16 +246,19 @@ def main():
         del od
         log(f"[bench] dense attention {dense_ms:.3f} ms")
 
-    # ---- roofline of the dominant kernel (attention), algorithmic FLOPs
+    # ---- roofline of the dominant kernel (the timed path's attention), algorithmic FLOPs
     bf16 = wl.dtype == "bf16"
     flops = attention_flops(bud, wl.Hq, wl.d)
-    achieved = flops / (steps_ms["attention"] * 1e-3) / 1e12
+    attn_step = "attention_indexed" if args.path == "fused" else "attention"
+    kname = ("attn_fwd_bf16" if bf16 else "attn_fwd_f32") + \
+        (f"<{wl.d}, true>" if args.path == "fused" else f"<{wl.d}, false>")
+    achieved = flops / (steps_ms[attn_step] * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
-    traffic = measured_traffic("attn_fwd_bf16", wl.name) if bf16 else None
+    traffic = measured_traffic(kname, wl.name) if bf16 else None
     roofline = {"bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic, "kernel": "attn_fwd_bf16" if bf16 else "attn_fwd_f32",
-                "flops_per_launch": flops, "avg_launch_ms": round(steps_ms["attention"], 4)}
+                "traffic": traffic, "kernel": kname,
+                "flops_per_launch": flops, "avg_launch_ms": round(steps_ms[attn_step], 4)}
 
     # HBM fractions of the byte-moving steps (algorithmic bytes)
     eb = 2 if bf16 else 4
@@ -239,14 +276,19 @@ def main():
         "select": 4 * heads * wl.L + 4 * Ksum + 4 * heads * wl.L,
         "gather": Ksum * row + 2 * uniq * row + 3 * Ksum * row + 4 * Ksum,
         "scatter": Ksum * row + heads * wl.L * row + 4 * heads * wl.L,
+        "zero_fill": 4 * heads * wl.L + (heads * wl.L - Ksum) * row,
     }
     kernels = {n: {"ms": round(steps_ms[n], 4),
                    "GB_s": round(hbm_bytes[n] / (steps_ms[n] * 1e-3) / 1e9, 1),
                    "hbm_frac": round(hbm_bytes[n] / (steps_ms[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                    "algorithmic_bytes": int(hbm_bytes[n])} for n in hbm_bytes}
-    kernels["attention"] = {"ms": round(steps_ms["attention"], 4),
-                            "TFLOP_s": round(achieved, 2), "mfma_frac": round(achieved / peak, 4)}
-    overhead = sum(steps_ms[n] for n in names if n != "attention")
+    for n in ("attention", "attention_indexed"):
+        tf = flops / (steps_ms[n] * 1e-3) / 1e12
+        kernels[n] = {"ms": round(steps_ms[n], 4), "TFLOP_s": round(tf, 2),
+                      "mfma_frac": round(tf / peak, 4)}
+    path_kernels = {"fused": ["score", "budget", "select", "zero_fill", "attention_indexed"],
+                    "steps": ["score", "budget", "select", "gather", "attention", "scatter"]}
+    overhead = sum(steps_ms[n] for n in path_kernels[args.path] if n != attn_step)
 
     out = {
         "metric": METRIC,
@@ -266,11 +308,13 @@ def main():
                    "parallelism": "none"},
         "budget": [int(x) for x in bud],
         "keep_frac": [round(int(x) / wl.L, 5) for x in bud],
+        "path": args.path,
+        "other_path": {"path": other, "ms_per_step": round(other_ms, 4)},
         "dense_ms": None if dense_ms is None else round(dense_ms, 4),
         "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 4),
-        "attention_speedup_vs_dense": None if dense_ms is None else round(dense_ms / steps_ms["attention"], 4),
-        "overhead_share": round(overhead / steps_ms["attention"], 4),
-        "steps_ms": {n: round(steps_ms[n], 4) for n in names},
+        "attention_speedup_vs_dense": None if dense_ms is None else round(dense_ms / steps_ms[attn_step], 4),
+        "overhead_share": round(overhead / steps_ms[attn_step], 4),
+        "path_kernels_ms": {p: {n: round(steps_ms[n], 4) for n in ks} for p, ks in path_kernels.items()},
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": None,

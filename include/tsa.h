@@ -86,6 +86,10 @@ size_t tsa_workspace_bytes(const tsa_problem* prob);
  * intermediate scores, rank map and the four compact per-head tensors. */
 size_t tsa_forward_workspace_bytes(const tsa_problem* prob);
 
+/* Scratch bytes needed by tsa_forward_fused: the step scratch plus the
+ * intermediate scores and rank map (no compact tensors). */
+size_t tsa_fused_workspace_bytes(const tsa_problem* prob);
+
 /* Proxy scoring ("Dynamic Token Coverage", scoring).  For every query head h
  * and proxy row r in [L-w, L): logits x_rj = <Q[b,h,r], K[b,g(h),j]>/sqrt(d)
  * over the causally visible keys j <= r, one softmax per row, and
@@ -149,6 +153,27 @@ tsa_status tsa_scatter(const tsa_problem* prob, const void* oc, const int32_t* r
 tsa_status tsa_forward(const tsa_problem* prob, const void* q, const void* k, const void* v,
                        void* o, int32_t* budget, int32_t* idx, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* Compression, attention and decompression of the selected rows in one
+ * kernel ("Core architecture", stages 1 and 2, with the dense attention on
+ * the compressed tensors between them).  For i < K_b, with t = idx[b,h,i]:
+ *   o[b,h,t] = sum_{j<=i} softmax_j(<Q[b,h,t], K[b,g(h),idx_j]>/sqrt(d)) V[b,g(h),idx_j]
+ * which is tsa_gather -> tsa_attention(kv_group=1) -> tsa_scatter on the
+ * selected rows, bit for bit.  q, o: [B,Hq,L,d]; k, v: [B,Hkv,L,d];
+ * idx: [B,Hq,L] int32 whose first K_b entries are ascending rows in [0,L)
+ * (as tsa_select writes them); budget: [B] int32 (device).  Only the
+ * selected rows of o are written; the other rows are left as they are. */
+tsa_status tsa_attention_indexed(const tsa_problem* prob, const void* q, const void* k,
+                                 const void* v, const int32_t* idx, const int32_t* budget, void* o,
+                                 void* stream);
+
+/* The whole op with the fused kernel: score -> budget -> select -> zero the
+ * unselected rows of o -> tsa_attention_indexed.  Same arguments and the
+ * same results, bit for bit, as tsa_forward, without the compact tensors:
+ * ws must hold tsa_fused_workspace_bytes(prob) bytes. */
+tsa_status tsa_forward_fused(const tsa_problem* prob, const void* q, const void* k, const void* v,
+                             void* o, int32_t* budget, int32_t* idx, void* ws, size_t ws_bytes,
+                             void* stream);
 
 #ifdef __cplusplus
 }

@@ -67,6 +67,11 @@ def test_workspace_sizes(lib):
     assert fwd >= step + 4 * 8 * 1000 * 2 + 4 * 8 * 1000 * 128 * 2
     assert lib.tsa_workspace_bytes(ctypes.byref(prob(Hkv=3))) == 0
     assert lib.tsa_workspace_bytes(None) == 0
+    # the fused forward needs the step scratch, scores and rank, not the compact tensors
+    fused = lib.tsa_fused_workspace_bytes(ctypes.byref(p))
+    assert step + 2 * 4 * 8 * 1000 <= fused < step + 2 * 4 * 8 * 1000 + 1024
+    assert fused % 256 == 0 and fused < fwd
+    assert lib.tsa_fused_workspace_bytes(None) == 0
 
 
 def test_workspace_scales_with_headline_shape(lib):
@@ -104,6 +109,9 @@ def _call_all(lib, p, ptr=FAKE, ws_bytes=1 << 40, kv_group=1):
         "attention": lib.tsa_attention(P, ptr, ptr, ptr, ptr, kv_group, ptr, None),
         "scatter": lib.tsa_scatter(P, ptr, ptr, ptr, None),
         "forward": lib.tsa_forward(P, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ws_bytes, None),
+        "attention_indexed": lib.tsa_attention_indexed(P, ptr, ptr, ptr, ptr, ptr, ptr, None),
+        "forward_fused": lib.tsa_forward_fused(P, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ws_bytes,
+                                               None),
     }
 
 
@@ -138,6 +146,9 @@ def test_workspace_too_small(lib):
         assert st == _lib.TSA_ERR_WORKSPACE
     fneed = lib.tsa_forward_workspace_bytes(P)
     assert lib.tsa_forward(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, fneed - 1, None) == \
+        _lib.TSA_ERR_WORKSPACE
+    uneed = lib.tsa_fused_workspace_bytes(P)
+    assert lib.tsa_forward_fused(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, uneed - 1, None) == \
         _lib.TSA_ERR_WORKSPACE
     # misaligned workspace
     assert lib.tsa_score(P, FAKE, FAKE, FAKE, FAKE + 16, need, None) == _lib.TSA_ERR_WORKSPACE

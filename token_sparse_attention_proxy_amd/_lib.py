@@ -17,7 +17,8 @@ TSA_F32, TSA_BF16 = 0, 1
 # Every symbol include/tsa.h declares.
 EXPORTS = ["tsa_status_string", "tsa_last_error", "tsa_version", "tsa_workspace_bytes",
            "tsa_forward_workspace_bytes", "tsa_score", "tsa_budget", "tsa_select", "tsa_gather",
-           "tsa_attention", "tsa_scatter", "tsa_forward"]
+           "tsa_attention", "tsa_scatter", "tsa_forward", "tsa_fused_workspace_bytes",
+           "tsa_attention_indexed", "tsa_forward_fused"]
 
 
 class TsaProblem(ctypes.Structure):
@@ -44,6 +45,9 @@ _SIGNATURES = {
     "tsa_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _i32, _vp, _vp]),
     "tsa_scatter": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp]),
     "tsa_forward": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "tsa_fused_workspace_bytes": (_sz, [_P]),
+    "tsa_attention_indexed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "tsa_forward_fused": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 _lib = None

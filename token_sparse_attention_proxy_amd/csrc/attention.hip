@@ -85,11 +85,16 @@ __device__ __forceinline__ int acc_key(int e, int half) {
   return 16 * (e >> 3) + 8 * half + 4 * ((e >> 2) & 1) + (e & 3);
 }
 
-template <int D>
+// IDX = false: q, k, v, o are dense per-head tensors and row i is row i.
+// IDX = true: compact row i of head (b,h) is sequence row idx[b,h,i]; Q, K, V
+// are read and O is written through the index set (compression, attention
+// and decompression of the selected rows in one pass).
+template <int D, bool IDX>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ budget,
-    uint16_t* __restrict__ o, int Hq, int Hk, int kv_group, int L, float c) {
+    const int32_t* __restrict__ idx, uint16_t* __restrict__ o, int Hq, int Hk, int kv_group,
+    int L, float c) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int KCH = kBN * D / 8 / kThreads;          // 16-byte K chunks per thread
   constexpr int VPAIRS = (kBN / 4) * (D / 8);          // (4-key group, 8-d chunk) pairs
@@ -98,6 +103,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   constexpr int NSUB = kBN / 32;                       // 32-key subtiles
   static_assert(KCH >= 1 && VPAIRS <= kThreads, "tile shape");
   __shared__ AttnSmem<D> sm;
+  __shared__ int idx_s[IDX ? 3 : 1][kBN];     // sequence rows of the next key tiles
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -110,7 +116,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   const int q0 = (nqb - 1 - int(blockIdx.x)) * kBM;    // heaviest blocks first
   if (q0 >= n) return;
 
-  const uint32_t head_bytes = uint32_t(n) * D * 2;
+  // Rows past the valid range read as 0 and are never written.  Indexed
+  // reads address the full sequence; compact rows >= n map to row L.
+  const uint32_t head_bytes = uint32_t(IDX ? L : n) * D * 2;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + int64_t(bh) * L * D, head_bytes);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (int64_t(b) * Hk + hk) * L * D, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + (int64_t(b) * Hk + hk) * L * D, head_bytes);
@@ -119,12 +127,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   const int qrow = wr0 + l32;                // the row this lane owns
   const int wdiag = wr0 / kBN;               // tile holding this wave's diagonal
 
+  const int32_t* __restrict__ idx_h = IDX ? idx + int64_t(bh) * L : nullptr;
+  const int qsrc = IDX ? (qrow < n ? idx_h[qrow] : L) : qrow;   // sequence row of this lane's query
+
   // Q^T as the B operand: lane holds q[qrow][16t + 8*half .. +8].
   bf16x8 qf[KS];
 #pragma unroll
   for (int t = 0; t < KS; ++t)
     qf[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rq, (qrow * D + 16 * t + 8 * half) * 2, 0, 0));
+                                           rq, (qsrc * D + 16 * t + 8 * half) * 2, 0, 0));
 
   const int kv_end = min(q0 + kBM, n);
   const int ntiles = (kv_end + kBN - 1) / kBN;
@@ -133,18 +144,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   u32x4 vreg[4];
   const int vkg = tid % (kBN / 4), vdc = tid / (kBN / 4);   // (key group, d chunk) of this thread
 
+  // Index ring: the sequence rows of tile t are fetched into a register two
+  // tiles ahead and published to LDS with the tile staging, so the K/V row
+  // loads of a tile never wait on the index load.
+  auto fetch_idx = [&](int tile) {
+    const int key = tile * kBN + tid;
+    return (IDX && tid < kBN && key < n) ? idx_h[key] : L;
+  };
+  auto put_idx = [&](int tile, int val) {
+    if (IDX && tid < kBN) idx_s[tile % 3][tid] = val;
+  };
+  auto src_row = [&](int tile, int row) {
+    return IDX ? idx_s[tile % 3][row] : tile * kBN + row;
+  };
   auto load_tile = [&](int tile) {
-    const int key0 = tile * kBN;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int ch = tid + kThreads * i;
       const int row = ch / (D / 8), col = ch % (D / 8);
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((key0 + row) * D + col * 8) * 2, 0, 0);
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (src_row(tile, row) * D + col * 8) * 2, 0, 0);
     }
     if (tid < VPAIRS) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((key0 + 4 * vkg + r) * D + vdc * 8) * 2, 0, 0);
+        vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, (src_row(tile, 4 * vkg + r) * D + vdc * 8) * 2, 0, 0);
     }
   };
   auto store_tile = [&](int buf) {
@@ -168,6 +191,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
         *reinterpret_cast<u32x2*>(&sm.vt[buf][8 * vdc + 2 * p + 1][4 * vkg]) = hi;
       }
     }
+  };
+  auto begin_walk = [&]() {
+    if (IDX) {
+      const int i0 = fetch_idx(0), i1 = fetch_idx(1);
+      put_idx(0, i0);
+      put_idx(1, i1);
+      __syncthreads();
+    }
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
   };
 
   const int krow = perm32(l32);
@@ -237,11 +271,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   for (int attempt = 0; attempt < 2; ++attempt) {
     if (attempt == 1) {
       float m = -INFINITY;
-      load_tile(0);
-      store_tile(0);
-      __syncthreads();
+      begin_walk();
       for (int tile = 0; tile < ntiles; ++tile) {
         const int buf = tile & 1;
+        const int inext = fetch_idx(tile + 2);
         if (tile + 1 < ntiles) load_tile(tile + 1);
         if (tile <= wdiag) {
           f32x16 sacc[NSUB];
@@ -250,6 +283,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
           m = fmaxf(m, tile_max(sacc));
         }
         if (tile + 1 < ntiles) store_tile(buf ^ 1);
+        put_idx(tile + 2, inext);
         __syncthreads();
       }
       m_ref = m * c;
@@ -257,11 +291,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
 #pragma unroll
     for (int i = 0; i < DT; ++i) oacc[i] = zero;
     l_run = 0.f;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    begin_walk();
     for (int tile = 0; tile < ntiles; ++tile) {
       const int buf = tile & 1;
+      const int inext = fetch_idx(tile + 2);
       if (tile + 1 < ntiles) load_tile(tile + 1);
       if (tile < wdiag && tile > 0) {
         f32x16 sacc[NSUB];              // hot path: no mask, no reductions
@@ -275,6 +308,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
         pv(buf, sacc);
       }
       if (tile + 1 < ntiles) store_tile(buf ^ 1);
+      put_idx(tile + 2, inext);
       __syncthreads();
     }
     const bool bad = !(sum_halves(l_run) <= kSumLimit);
@@ -290,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
       u32x2 pk;
       pk.x = pack_bf16x2(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
       pk.y = pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
-      __builtin_amdgcn_raw_buffer_store_b64(pk, ro, (qrow * D + 32 * dt + 8 * g + 4 * half) * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(pk, ro, (qsrc * D + 32 * dt + 8 * g + 4 * half) * 2, 0, 0);
     }
 }
 
@@ -298,13 +332,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
 constexpr int kF32Rows = 64;    // query rows per workgroup (one per thread)
 constexpr int kF32Keys = 32;    // keys per LDS tile
 
-template <int D>
+template <int D, bool IDX>
 __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const int32_t* __restrict__ budget, float* __restrict__ o, int Hq, int Hk, int kv_group, int L,
-    float c) {
+    const int32_t* __restrict__ budget, const int32_t* __restrict__ idx, float* __restrict__ o,
+    int Hq, int Hk, int kv_group, int L, float c) {
   __shared__ float ks[kF32Keys][D];
   __shared__ float vs[kF32Keys][D];
+  __shared__ int rows_s[kF32Keys];
   const int bh = blockIdx.y;
   const int b = bh / Hq, h = bh % Hq;
   const int hk = h / kv_group;
@@ -315,21 +350,31 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32(
   const int i = q0 + threadIdx.x;
   const int64_t qbase = int64_t(bh) * L * D;
   const int64_t kvbase = (int64_t(b) * Hk + hk) * L * D;
+  const int32_t* __restrict__ idx_h = IDX ? idx + int64_t(bh) * L : nullptr;
+  // sequence row of this query; -1 past the budget (or for an index outside [0, L))
+  int qsrc = i < n ? (IDX ? idx_h[i] : i) : -1;
+  if (qsrc >= L) qsrc = -1;
   float qr[D], acc[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
-    qr[e] = i < n ? q[qbase + int64_t(i) * D + e] : 0.f;
+    qr[e] = qsrc >= 0 ? q[qbase + int64_t(qsrc) * D + e] : 0.f;
     acc[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
   const int kv_end = min(q0 + kF32Rows, n);
   for (int key0 = 0; key0 < kv_end; key0 += kF32Keys) {
     __syncthreads();
+    if (threadIdx.x < kF32Keys) {
+      const int key = key0 + threadIdx.x;
+      const int src = key < n ? (IDX ? idx_h[key] : key) : -1;
+      rows_s[threadIdx.x] = src < L ? src : -1;
+    }
+    __syncthreads();
     for (int e = threadIdx.x; e < kF32Keys * D; e += kF32Rows) {
       const int r = e / D, col = e % D;
-      const bool ok = key0 + r < n;
-      ks[r][col] = ok ? k[kvbase + int64_t(key0 + r) * D + col] : 0.f;
-      vs[r][col] = ok ? v[kvbase + int64_t(key0 + r) * D + col] : 0.f;
+      const int src = rows_s[r];
+      ks[r][col] = src >= 0 ? k[kvbase + int64_t(src) * D + col] : 0.f;
+      vs[r][col] = src >= 0 ? v[kvbase + int64_t(src) * D + col] : 0.f;
     }
     __syncthreads();
     float x[kF32Keys];
@@ -356,45 +401,56 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32(
     }
     m = m_new;
   }
-  if (i < n) {
+  if (qsrc >= 0) {
     const float inv = 1.0f / l;
 #pragma unroll
-    for (int e = 0; e < D; ++e) o[qbase + int64_t(i) * D + e] = acc[e] * inv;
+    for (int e = 0; e < D; ++e) o[qbase + int64_t(qsrc) * D + e] = acc[e] * inv;
   }
 }
 
-template <int D>
+template <int D, bool IDX>
 hipError_t run_bf16(const Shape& sh, const void* q, const void* k, const void* v,
-                    const int32_t* budget, int kv_group, void* o, hipStream_t st) {
+                    const int32_t* budget, const int32_t* idx, int kv_group, void* o,
+                    hipStream_t st) {
   const float c = kLog2e / sqrtf(float(D));
   dim3 grid((sh.L + kBM - 1) / kBM, sh.B * sh.Hq);
-  attn_fwd_bf16<D><<<grid, kThreads, 0, st>>>(
+  attn_fwd_bf16<D, IDX><<<grid, kThreads, 0, st>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), budget, static_cast<uint16_t*>(o), sh.Hq,
+      static_cast<const uint16_t*>(v), budget, idx, static_cast<uint16_t*>(o), sh.Hq,
       sh.Hq / kv_group, kv_group, sh.L, c);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool IDX>
 hipError_t run_f32(const Shape& sh, const void* q, const void* k, const void* v,
-                   const int32_t* budget, int kv_group, void* o, hipStream_t st) {
+                   const int32_t* budget, const int32_t* idx, int kv_group, void* o,
+                   hipStream_t st) {
   const float c = kLog2e / sqrtf(float(D));
   dim3 grid((sh.L + kF32Rows - 1) / kF32Rows, sh.B * sh.Hq);
-  attn_fwd_f32<D><<<grid, kF32Rows, 0, st>>>(
+  attn_fwd_f32<D, IDX><<<grid, kF32Rows, 0, st>>>(
       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-      budget, static_cast<float*>(o), sh.Hq, sh.Hq / kv_group, kv_group, sh.L, c);
+      budget, idx, static_cast<float*>(o), sh.Hq, sh.Hq / kv_group, kv_group, sh.L, c);
   return hipGetLastError();
+}
+
+template <bool IDX>
+hipError_t run(const Shape& sh, const void* q, const void* k, const void* v,
+               const int32_t* budget, const int32_t* idx, int kv_group, void* o,
+               hipStream_t st) {
+  if (sh.dtype == TSA_BF16)
+    return sh.d == 128 ? run_bf16<128, IDX>(sh, q, k, v, budget, idx, kv_group, o, st)
+                       : run_bf16<64, IDX>(sh, q, k, v, budget, idx, kv_group, o, st);
+  return sh.d == 128 ? run_f32<128, IDX>(sh, q, k, v, budget, idx, kv_group, o, st)
+                     : run_f32<64, IDX>(sh, q, k, v, budget, idx, kv_group, o, st);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const void* v,
-                            const int32_t* budget, int kv_group, void* o, hipStream_t st) {
-  if (sh.dtype == TSA_BF16)
-    return sh.d == 128 ? run_bf16<128>(sh, q, k, v, budget, kv_group, o, st)
-                       : run_bf16<64>(sh, q, k, v, budget, kv_group, o, st);
-  return sh.d == 128 ? run_f32<128>(sh, q, k, v, budget, kv_group, o, st)
-                     : run_f32<64>(sh, q, k, v, budget, kv_group, o, st);
+                            const int32_t* budget, const int32_t* idx, int kv_group, void* o,
+                            hipStream_t st) {
+  return idx ? run<true>(sh, q, k, v, budget, idx, kv_group, o, st)
+             : run<false>(sh, q, k, v, budget, nullptr, kv_group, o, st);
 }
 
 }  // namespace tsa

@@ -7,6 +7,10 @@
 // Both are pure byte movement: rows are copied as 16-byte vectors, one row
 // per group of lanes.  The scatter is destination-driven, so each output
 // row is written exactly once (copied or zero-filled) and coalesced.
+//
+// zero_unselected: o[b,h,j] = 0 for every j with rank_j < 0.  It is the part
+// of decompression left when the attention kernel itself writes the
+// selected rows to their sequence positions.
 #include "tsa_device.h"
 #include "tsa_internal.h"
 
@@ -72,6 +76,26 @@ __global__ __launch_bounds__(kThreads) void scatter_rows(const u32x4* __restrict
 }
 
 template <int VPR>
+__global__ __launch_bounds__(kThreads) void zero_rows(const int32_t* __restrict__ rank,
+                                                      u32x4* __restrict__ o, int L) {
+  constexpr int kRowsPerPass = kThreads / VPR;
+  const int bh = blockIdx.y;
+  const int j0 = blockIdx.x * kRowsPerBlock;
+  const int sub = threadIdx.x / VPR, vec = threadIdx.x % VPR;
+  const int64_t hrow = int64_t(bh) * L;
+  for (int j = j0 + sub; j < min(j0 + kRowsPerBlock, L); j += kRowsPerPass) {
+    if (rank[hrow + j] < 0) o[(hrow + j) * VPR + vec] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int VPR>
+hipError_t zero_vpr(const Shape& sh, const int32_t* rank, void* o, hipStream_t st) {
+  dim3 grid((sh.L + kRowsPerBlock - 1) / kRowsPerBlock, sh.B * sh.Hq);
+  zero_rows<VPR><<<grid, kThreads, 0, st>>>(rank, static_cast<u32x4*>(o), sh.L);
+  return hipGetLastError();
+}
+
+template <int VPR>
 hipError_t gather_vpr(const Shape& sh, const void* q, const void* k, const void* v,
                       const int32_t* idx, const int32_t* budget, void* qc, void* kc, void* vc,
                       hipStream_t st) {
@@ -101,6 +125,15 @@ hipError_t launch_gather(const Shape& sh, const void* q, const void* k, const vo
     case 8: return gather_vpr<8>(sh, q, k, v, idx, budget, qc, kc, vc, st);
     case 16: return gather_vpr<16>(sh, q, k, v, idx, budget, qc, kc, vc, st);
     case 32: return gather_vpr<32>(sh, q, k, v, idx, budget, qc, kc, vc, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_zero_unselected(const Shape& sh, const int32_t* rank, void* o, hipStream_t st) {
+  switch (sh.row_bytes() / 16) {
+    case 8: return zero_vpr<8>(sh, rank, o, st);
+    case 16: return zero_vpr<16>(sh, rank, o, st);
+    case 32: return zero_vpr<32>(sh, rank, o, st);
   }
   return hipErrorInvalidValue;
 }

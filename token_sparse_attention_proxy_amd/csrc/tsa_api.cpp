@@ -124,6 +124,7 @@ FwdWs fwd_ws_layout(const Shape& s) {
   off = align256(off + sizeof(float) * heads * s.L);
   f.rank = off;
   off = align256(off + sizeof(int32_t) * heads * s.L);
+  f.fused_total = off;
   const size_t tens = heads * size_t(s.L) * size_t(s.row_bytes());
   f.qc = off;
   off = align256(off + tens);
@@ -166,6 +167,12 @@ size_t tsa_forward_workspace_bytes(const tsa_problem* prob) {
   tsa::Shape s;
   if (check_problem(prob, &s) != TSA_OK) return 0;
   return tsa::fwd_ws_layout(s).total;
+}
+
+size_t tsa_fused_workspace_bytes(const tsa_problem* prob) {
+  tsa::Shape s;
+  if (check_problem(prob, &s) != TSA_OK) return 0;
+  return tsa::fwd_ws_layout(s).fused_total;
 }
 
 tsa_status tsa_score(const tsa_problem* prob, const void* q, const void* k, float* s, void* ws,
@@ -238,8 +245,9 @@ tsa_status tsa_attention(const tsa_problem* prob, const void* q, const void* k, 
   if (kv_group < 1 || sh.Hq % kv_group != 0)
     return fail(TSA_ERR_INVALID_ARG, "kv_group=%d must be >= 1 and divide Hq=%d", kv_group, sh.Hq);
   if (fault_injected()) return injected("tsa_attention");
-  return launched(tsa::launch_attention(sh, q, k, v, budget, kv_group, o, hipStream_t(stream)),
-                  "tsa_attention");
+  return launched(
+      tsa::launch_attention(sh, q, k, v, budget, nullptr, kv_group, o, hipStream_t(stream)),
+      "tsa_attention");
 }
 
 tsa_status tsa_scatter(const tsa_problem* prob, const void* oc, const int32_t* rank, void* o,
@@ -283,10 +291,59 @@ tsa_status tsa_forward(const tsa_problem* prob, const void* q, const void* k, co
     return launched(err, "tsa_forward/select");
   if ((err = tsa::launch_gather(sh, q, k, v, idx, budget, qc, kc, vc, st)) != hipSuccess)
     return launched(err, "tsa_forward/gather");
-  if ((err = tsa::launch_attention(sh, qc, kc, vc, budget, 1, oc, st)) != hipSuccess)
+  if ((err = tsa::launch_attention(sh, qc, kc, vc, budget, nullptr, 1, oc, st)) != hipSuccess)
     return launched(err, "tsa_forward/attention");
   if ((err = tsa::launch_scatter(sh, oc, rank, o, st)) != hipSuccess)
     return launched(err, "tsa_forward/scatter");
+  return ok();
+}
+
+tsa_status tsa_attention_indexed(const tsa_problem* prob, const void* q, const void* k,
+                                 const void* v, const int32_t* idx, const int32_t* budget, void* o,
+                                 void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_problem(prob, &sh));
+  TSA_TRY(check_ptr(q, "q"));
+  TSA_TRY(check_ptr(k, "k"));
+  TSA_TRY(check_ptr(v, "v"));
+  TSA_TRY(check_ptr(idx, "idx"));
+  TSA_TRY(check_ptr(budget, "budget"));
+  TSA_TRY(check_ptr(o, "o"));
+  if (fault_injected()) return injected("tsa_attention_indexed");
+  return launched(tsa::launch_attention(sh, q, k, v, budget, idx, sh.Hq / sh.Hkv, o,
+                                        hipStream_t(stream)),
+                  "tsa_attention_indexed");
+}
+
+tsa_status tsa_forward_fused(const tsa_problem* prob, const void* q, const void* k, const void* v,
+                             void* o, int32_t* budget, int32_t* idx, void* ws, size_t ws_bytes,
+                             void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_problem(prob, &sh));
+  TSA_TRY(check_ptr(q, "q"));
+  TSA_TRY(check_ptr(k, "k"));
+  TSA_TRY(check_ptr(v, "v"));
+  TSA_TRY(check_ptr(o, "o"));
+  TSA_TRY(check_ptr(budget, "budget"));
+  TSA_TRY(check_ptr(idx, "idx"));
+  const tsa::FwdWs f = tsa::fwd_ws_layout(sh);
+  TSA_TRY(check_ws(ws, ws_bytes, f.fused_total));
+  if (fault_injected()) return injected("tsa_forward_fused");
+  char* base = static_cast<char*>(ws);
+  hipStream_t st = hipStream_t(stream);
+  float* scores = reinterpret_cast<float*>(base + f.scores);
+  int32_t* rank = reinterpret_cast<int32_t*>(base + f.rank);
+  hipError_t err;
+  if ((err = tsa::launch_score(sh, q, k, scores, base, st)) != hipSuccess)
+    return launched(err, "tsa_forward_fused/score");
+  if ((err = tsa::launch_budget(sh, scores, budget, base, st)) != hipSuccess)
+    return launched(err, "tsa_forward_fused/budget");
+  if ((err = tsa::launch_select(sh, scores, budget, idx, rank, base, st)) != hipSuccess)
+    return launched(err, "tsa_forward_fused/select");
+  if ((err = tsa::launch_zero_unselected(sh, rank, o, st)) != hipSuccess)
+    return launched(err, "tsa_forward_fused/zero");
+  if ((err = tsa::launch_attention(sh, q, k, v, budget, idx, sh.Hq / sh.Hkv, o, st)) != hipSuccess)
+    return launched(err, "tsa_forward_fused/attention");
   return ok();
 }
 

@@ -43,6 +43,7 @@ struct FwdWs {
   StepWs step;
   size_t scores;      // float [B*Hq*L]
   size_t rank;        // int32 [B*Hq*L]
+  size_t fused_total; // end of rank: all the fused forward needs
   size_t qc, kc, vc, oc;   // dtype [B*Hq*L*d] each
   size_t total;
 };
@@ -59,8 +60,14 @@ hipError_t launch_select(const Shape& s, const float* scores, const int32_t* bud
 hipError_t launch_gather(const Shape& s, const void* q, const void* k, const void* v,
                          const int32_t* idx, const int32_t* budget, void* qc, void* kc,
                          void* vc, hipStream_t st);
+// idx == nullptr: q, k, v, o hold rows 0..n-1 of each head (dense or
+// compact).  Otherwise they are full-length sequence tensors and compact
+// row i of head (b,h) is sequence row idx[b,h,i]; only those rows of o are
+// written.
 hipError_t launch_attention(const Shape& s, const void* q, const void* k, const void* v,
-                            const int32_t* budget, int kv_group, void* o, hipStream_t st);
+                            const int32_t* budget, const int32_t* idx, int kv_group, void* o,
+                            hipStream_t st);
+hipError_t launch_zero_unselected(const Shape& s, const int32_t* rank, void* o, hipStream_t st);
 hipError_t launch_scatter(const Shape& s, const void* oc, const int32_t* rank, void* o,
                           hipStream_t st);
 

@@ -2,15 +2,18 @@
 
 Two sub-commands, meant to run under rocprofv3 and after it:
 
-  python -m token_sparse_attention_proxy_amd.profiling run --workload NAME
+  python -m token_sparse_attention_proxy_amd.profiling run --workload NAME --path P
       Runs, in one process: a plain device-to-device copy of COPY_BYTES
-      (calibration), then the attention kernel on the compact shape of the
-      workload with its measured budget (inputs are random bf16 made on the
-      GPU; traffic depends on shapes and the budget, not on values).  Run it
-      twice under ``rocprofv3 --pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``.
+      (calibration), then the attention of one path:
+        compact: the attention kernel alone on the compact shape of the
+          workload with its measured budget (random bf16 inputs made on the
+          GPU; traffic depends on shapes and the budget, not on values);
+        fused: tsa_forward_fused on the workload's own seeded inputs (the
+          indexed attention's reads follow the real index sets).
+      Run it twice under ``rocprofv3 --pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``.
 
   python -m token_sparse_attention_proxy_amd.profiling summarize \\
-        --fetch DIR --write DIR --workload NAME --budget K [--out profiles/traffic.json]
+        --fetch DIR --write DIR --workload NAME --budget K --path P [--out profiles/traffic.json]
       Reads the two counter CSVs, scales each counter by what it reads for
       the copy (bytes moved / counter bytes), and records the attention
       kernel's HBM bytes per launch, keyed by the kernel source hash, so that
@@ -44,16 +47,27 @@ def cmd_run(args):
 
     wl = inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.path == "fused":
+        q, k, v = inputs.make_qkv(wl)
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        qd, kd, vd = (torch.from_numpy(x).to(tdt).to(dev) for x in (q, k, v))
+        del q, k, v
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     dst.copy_(src)                       # calibration: COPY_BYTES read, COPY_BYTES written
     torch.cuda.synchronize()
     del src, dst
+    prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, wl.taus[0], wl.dtype)
+    if args.path == "fused":
+        o, bud, _ = T.tsa_forward_fused(prob, qd, kd, vd)
+        torch.cuda.synchronize()
+        print(f"ran copy of {COPY_BYTES} B and tsa_forward_fused on {wl.name}, "
+              f"budget {bud.cpu().tolist()}")
+        return
     g = torch.Generator(device=dev).manual_seed(0)
     shape = (wl.B, wl.Hq, wl.L, wl.d)
     q, k, v = (torch.randn(shape, device=dev, generator=g).to(torch.bfloat16) for _ in range(3))
     bud = torch.full((wl.B,), args.budget, dtype=torch.int32, device=dev)
-    prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, wl.taus[0], wl.dtype)
     o = torch.empty_like(q)
     T.tsa_attention(prob, q, k, v, bud, 1, o)
     torch.cuda.synchronize()
@@ -86,12 +100,14 @@ def cmd_summarize(args):
     copy_w = max(v for n, v in write if "attn_fwd" not in n) * 1024.0
     f_scale = COPY_BYTES / copy_f
     w_scale = COPY_BYTES / copy_w
-    af = _pick(fetch, "attn_fwd")
-    aw = _pick(write, "attn_fwd")
+    kname = f"attn_fwd_bf16<{args.d}, {'true' if args.path == 'fused' else 'false'}>"
+    af = _pick(fetch, kname)
+    aw = _pick(write, kname)
     fetch_b = sum(af) / len(af) * 1024.0 * f_scale
     write_b = sum(aw) / len(aw) * 1024.0 * w_scale
     entry = {
         "source_sha": source_sha(),
+        "path": args.path,
         "budget": args.budget,
         "fetch_bytes_per_launch": fetch_b,
         "write_bytes_per_launch": write_b,
@@ -104,7 +120,7 @@ def cmd_summarize(args):
     if os.path.exists(args.out):
         with open(args.out) as f:
             tab = json.load(f)
-    tab.setdefault("attn_fwd_bf16", {})[args.workload] = entry
+    tab.setdefault(kname, {})[args.workload] = entry
     with open(args.out, "w") as f:
         json.dump(tab, f, indent=1, sort_keys=True)
     print(json.dumps(entry, indent=1))
@@ -116,12 +132,15 @@ def main():
     r = sub.add_parser("run")
     r.add_argument("--workload", default="llama8b_bf16_L128k")
     r.add_argument("--budget", type=int, default=123997)
+    r.add_argument("--path", choices=["compact", "fused"], default="fused")
     r.set_defaults(fn=cmd_run)
     s = sub.add_parser("summarize")
     s.add_argument("--fetch", required=True)
     s.add_argument("--write", required=True)
     s.add_argument("--workload", default="llama8b_bf16_L128k")
     s.add_argument("--budget", type=int, default=123997)
+    s.add_argument("--path", choices=["compact", "fused"], default="fused")
+    s.add_argument("--d", type=int, default=128)
     s.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
     s.set_defaults(fn=cmd_summarize)
     args = ap.parse_args()

@@ -71,6 +71,10 @@ def forward_workspace_bytes(prob: Problem) -> int:
     return int(_lib.load().tsa_forward_workspace_bytes(ctypes.byref(prob.c())))
 
 
+def fused_workspace_bytes(prob: Problem) -> int:
+    return int(_lib.load().tsa_fused_workspace_bytes(ctypes.byref(prob.c())))
+
+
 def _ws(prob: Problem, like: torch.Tensor, ws: Optional[torch.Tensor], nbytes: int) -> torch.Tensor:
     if ws is None:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=like.device)
@@ -153,12 +157,37 @@ def tsa_forward(prob: Problem, q, k, v, o=None, budget=None, idx=None, ws=None):
     return o, budget, idx
 
 
-def forward(q, k, v, w: int, tau: float):
+def tsa_attention_indexed(prob: Problem, q, k, v, idx, budget, o=None):
+    """Writes only the selected rows of o; a new o is zero-filled first."""
+    lib = _lib.load()
+    p = prob.c()
+    o = torch.zeros_like(q) if o is None else o
+    check(lib.tsa_attention_indexed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                                    _ptr(budget), _ptr(o), _stream(q.device)),
+          "tsa_attention_indexed")
+    return o
+
+
+def tsa_forward_fused(prob: Problem, q, k, v, o=None, budget=None, idx=None, ws=None):
+    lib = _lib.load()
+    p = prob.c()
+    o = _empty(q.shape, q.dtype, q) if o is None else o
+    budget = _empty((prob.B,), torch.int32, q) if budget is None else budget
+    idx = _empty((prob.B, prob.Hq, prob.L), torch.int32, q) if idx is None else idx
+    ws = _ws(prob, q, ws, fused_workspace_bytes(prob))
+    check(lib.tsa_forward_fused(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                _ptr(budget), _ptr(idx), _ptr(ws), ws.numel(),
+                                _stream(q.device)), "tsa_forward_fused")
+    return o, budget, idx
+
+
+def forward(q, k, v, w: int, tau: float, fused: bool = False):
     """The whole op on torch device tensors: returns (o, budget, idx)."""
     prob = Problem.from_qkv(q, k, w, tau)
-    return tsa_forward(prob, q, k, v)
+    return (tsa_forward_fused if fused else tsa_forward)(prob, q, k, v)
 
 
-__all__ = ["Problem", "TsaError", "workspace_bytes", "forward_workspace_bytes", "tsa_score",
-           "tsa_budget", "tsa_select", "tsa_gather", "tsa_attention", "tsa_scatter",
-           "tsa_forward", "forward"]
+__all__ = ["Problem", "TsaError", "workspace_bytes", "forward_workspace_bytes",
+           "fused_workspace_bytes", "tsa_score", "tsa_budget", "tsa_select", "tsa_gather",
+           "tsa_attention", "tsa_scatter", "tsa_forward", "tsa_attention_indexed",
+           "tsa_forward_fused", "forward"]
