@@ -199,6 +199,7 @@ def main():
         "gather": lambda: T.tsa_gather(prob, qd, kd, vd, idx, budget, qc, kc, vc),
         "attention": lambda: T.tsa_attention(prob, qc, kc, vc, budget, 1, oc),
         "scatter": lambda: T.tsa_scatter(prob, oc, rank, o),
+        "zero_fill": lambda: T.tsa_zero_unselected(prob, rank, o),
         "attention_indexed": lambda: T.tsa_attention_indexed(prob, qd, kd, vd, idx, budget, o),
     }
     names = list(calls)
@@ -215,17 +216,6 @@ def main():
             for i, n in enumerate(names):
                 acc[n] += ev[i].elapsed_time(ev[i + 1])
     steps_ms = {n: acc[n] / reps for n in names}
-    # the fused path's zero fill is internal to tsa_forward_fused: its time is
-    # the fused step (event-timed) minus the four kernels timed above
-    ef0, ef1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ef0.record(st)
-    for _ in range(reps):
-        paths["fused"]()
-    ef1.record(st)
-    torch.cuda.synchronize()
-    fused_ev_ms = ef0.elapsed_time(ef1) / reps
-    steps_ms["zero_fill"] = max(0.0, fused_ev_ms - sum(steps_ms[n] for n in
-                                                       ("score", "budget", "select", "attention_indexed")))
     log("[bench] kernels ms: " + ", ".join(f"{n} {steps_ms[n]:.3f}" for n in steps_ms))
 
     # ---- dense causal attention baseline (same kernel, GQA head map)

@@ -112,6 +112,7 @@ def _call_all(lib, p, ptr=FAKE, ws_bytes=1 << 40, kv_group=1):
         "attention_indexed": lib.tsa_attention_indexed(P, ptr, ptr, ptr, ptr, ptr, ptr, None),
         "forward_fused": lib.tsa_forward_fused(P, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ws_bytes,
                                                None),
+        "zero_unselected": lib.tsa_zero_unselected(P, ptr, ptr, None),
     }
 
 

@@ -153,3 +153,23 @@ def test_forward_fused_full_size(name):
                     sample_rows=sample, seed=7)
     del o, budget, idx, qd, kd, vd
     torch.cuda.empty_cache()
+
+
+def test_fused_steps_compose_to_forward_fused():
+    """score -> budget -> select -> zero_unselected -> attention_indexed, called
+    one by one, give tsa_forward_fused's result bit for bit."""
+    wl = SMALL[1]
+    say("case fused steps == forward_fused")
+    q, k, v = inputs.make_qkv(wl)
+    prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, 0.2, wl.dtype)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    o, budget, idx = T.tsa_forward_fused(prob, qd, kd, vd)
+    s = T.tsa_score(prob, qd, kd)
+    bud = T.tsa_budget(prob, s)
+    idx2, rank = T.tsa_select(prob, s, bud)
+    o2 = torch.full_like(qd, float("nan"))
+    T.tsa_zero_unselected(prob, rank, o2)
+    T.tsa_attention_indexed(prob, qd, kd, vd, idx2, bud, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(budget, bud) and torch.equal(idx, idx2)
+    assert torch.equal(_bits(o), _bits(o2))

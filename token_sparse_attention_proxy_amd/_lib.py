@@ -18,7 +18,7 @@ TSA_F32, TSA_BF16 = 0, 1
 EXPORTS = ["tsa_status_string", "tsa_last_error", "tsa_version", "tsa_workspace_bytes",
            "tsa_forward_workspace_bytes", "tsa_score", "tsa_budget", "tsa_select", "tsa_gather",
            "tsa_attention", "tsa_scatter", "tsa_forward", "tsa_fused_workspace_bytes",
-           "tsa_attention_indexed", "tsa_forward_fused"]
+           "tsa_attention_indexed", "tsa_forward_fused", "tsa_zero_unselected"]
 
 
 class TsaProblem(ctypes.Structure):
@@ -48,6 +48,7 @@ _SIGNATURES = {
     "tsa_fused_workspace_bytes": (_sz, [_P]),
     "tsa_attention_indexed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tsa_forward_fused": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "tsa_zero_unselected": (ctypes.c_int, [_P, _vp, _vp, _vp]),
 }
 
 _lib = None

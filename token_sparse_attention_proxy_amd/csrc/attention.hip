@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   constexpr int NSUB = kBN / 32;                       // 32-key subtiles
   static_assert(KCH >= 1 && VPAIRS <= kThreads, "tile shape");
   __shared__ AttnSmem<D> sm;
-  __shared__ int idx_s[IDX ? 3 : 1][kBN];     // sequence rows of the next key tiles
+  __shared__ int idx_s[IDX ? 2 : 1][kBN];     // sequence rows of upcoming key tiles
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -144,30 +144,40 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   u32x4 vreg[4];
   const int vkg = tid % (kBN / 4), vdc = tid / (kBN / 4);   // (key group, d chunk) of this thread
 
-  // Index ring: the sequence rows of tile t are fetched into a register two
-  // tiles ahead and published to LDS with the tile staging, so the K/V row
-  // loads of a tile never wait on the index load.
+  // Indexed staging.  The sequence rows of key tile t are fetched from HBM
+  // (one per thread of wave 0) at the top of iteration t-4, published to a
+  // two-slot LDS ring at the top of iteration t-3, and read into this
+  // thread's row registers early in iteration t-2, under its MFMA work.  The
+  // K/V loads of tile t, issued at the top of iteration t-1, then wait on
+  // nothing, and no index work sits before a barrier.
+  int krs[KCH], vrs[4];      // sequence rows of the K and V rows this thread stages next
   auto fetch_idx = [&](int tile) {
     const int key = tile * kBN + tid;
     return (IDX && tid < kBN && key < n) ? idx_h[key] : L;
   };
   auto put_idx = [&](int tile, int val) {
-    if (IDX && tid < kBN) idx_s[tile % 3][tid] = val;
+    if (IDX && tid < kBN) idx_s[tile & 1][tid] = val;
   };
-  auto src_row = [&](int tile, int row) {
-    return IDX ? idx_s[tile % 3][row] : tile * kBN + row;
-  };
-  auto load_tile = [&](int tile) {
+  auto read_rows = [&](int tile) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + kThreads * i;
-      const int row = ch / (D / 8), col = ch % (D / 8);
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (src_row(tile, row) * D + col * 8) * 2, 0, 0);
+      const int row = (tid + kThreads * i) / (D / 8);
+      krs[i] = IDX ? idx_s[tile & 1][row] : tile * kBN + row;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vrs[r] = IDX ? idx_s[tile & 1][4 * vkg + r] : tile * kBN + 4 * vkg + r;
+  };
+  auto load_tile = [&](int tile) {
+    if (!IDX) read_rows(tile);
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int col = (tid + kThreads * i) % (D / 8);
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (krs[i] * D + col * 8) * 2, 0, 0);
     }
     if (tid < VPAIRS) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, (src_row(tile, 4 * vkg + r) * D + vdc * 8) * 2, 0, 0);
+        vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, (vrs[r] * D + vdc * 8) * 2, 0, 0);
     }
   };
   auto store_tile = [&](int buf) {
@@ -192,17 +202,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
       }
     }
   };
+  int held = L;               // index entry fetched for the ring, published next iteration
   auto begin_walk = [&]() {
     if (IDX) {
-      const int i0 = fetch_idx(0), i1 = fetch_idx(1);
+      const int i0 = fetch_idx(0), i1 = fetch_idx(1), i2 = fetch_idx(2);
+      held = fetch_idx(3);
       put_idx(0, i0);
       put_idx(1, i1);
       __syncthreads();
+      read_rows(0);
+      load_tile(0);
+      read_rows(1);
+      __syncthreads();                 // slot 0 is free again
+      put_idx(2, i2);
+    } else {
+      load_tile(0);
     }
-    load_tile(0);
     store_tile(0);
     __syncthreads();
   };
+
 
   const int krow = perm32(l32);
   const f32x16 zero = {};
@@ -267,6 +286,65 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
       }
   };
 
+  // The same tile as qk + pv (same operations in the same accumulation
+  // orders, so the same bits) for tiles below the diagonal, written as one
+  // software pipeline in program order: LDS operand reads run PF ahead of
+  // their MFMA, the S^T chain of subtile q+1 carries the exp/convert work of
+  // subtile q, and the PV MFMAs of the first subtiles carry that of the last.
+  auto hot = [&](int buf) {
+    constexpr int NQK = NSUB * KS;            // S^T MFMAs, chain after chain
+    constexpr int NPV = 2 * NSUB * DT;        // O^T MFMAs, kk-major
+    constexpr int NR = NQK + NPV;             // operand reads, in MFMA order
+    constexpr int PF = 2;
+    constexpr int LAST = NSUB - 1;
+    constexpr int LAST_SLOT = 2 * LAST * DT;  // PV MFMAs that carry the last subtile's softmax
+    static_assert(LAST >= 1 && 8 % KS == 0 && 8 % LAST_SLOT == 0, "pipeline shape");
+    const float mneg = -m_ref;
+    const uint16_t* kbase = &sm.k[buf][krow][8 * half];
+    const uint16_t* vbase = &sm.vt[buf][l32][8 * half];
+    auto rd = [&](int r) {
+      if (r < NQK)
+        return *reinterpret_cast<const bf16x8*>(kbase + 32 * (r / KS) * (D + kKPad) + 16 * (r % KS));
+      const int j = r - NQK;
+      return *reinterpret_cast<const bf16x8*>(vbase + 32 * (j % DT) * (kBN + kVPad) + 16 * (j / DT));
+    };
+    f32x16 sacc[NSUB];
+    u32x4 pk[2 * NSUB];
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    auto softmax_pair = [&](int sb, int p) {  // elements 2p, 2p+1 of subtile sb
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[sb][2 * p], c, mneg));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[sb][2 * p + 1], c, mneg));
+      ls[(2 * p) & 3] += p0;
+      ls[(2 * p + 1) & 3] += p1;
+      pk[2 * sb + p / 4][p % 4] = pack_bf16x2(p0, p1);
+    };
+    bf16x8 ring[PF + 1];
+#pragma unroll
+    for (int r = 0; r < PF; ++r) ring[r] = rd(r);
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      if (m + PF < NR) ring[(m + PF) % (PF + 1)] = rd(m + PF);
+      const bf16x8 a = ring[m % (PF + 1)];
+      if (m < NQK) {
+        const int sb = m / KS, t = m % KS;
+        sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? zero : sacc[sb], 0, 0, 0);
+        if (sb >= 1) {                        // softmax of subtile sb-1, 8/KS pairs per MFMA
+#pragma unroll
+          for (int p = t * (8 / KS); p < (t + 1) * (8 / KS); ++p) softmax_pair(sb - 1, p);
+        }
+      } else {
+        const int j = m - NQK, kk = j / DT, dt = j % DT;
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pk[kk]),
+                                                           oacc[dt], 0, 0, 0);
+        if (j < LAST_SLOT) {
+#pragma unroll
+          for (int p = j * (8 / LAST_SLOT); p < (j + 1) * (8 / LAST_SLOT); ++p) softmax_pair(LAST, p);
+        }
+      }
+    }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+
   // attempt 0: reference = max of the first key tile; attempt 1 (rare): exact row max.
   for (int attempt = 0; attempt < 2; ++attempt) {
     if (attempt == 1) {
@@ -274,8 +352,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
       begin_walk();
       for (int tile = 0; tile < ntiles; ++tile) {
         const int buf = tile & 1;
-        const int inext = fetch_idx(tile + 2);
+        put_idx(tile + 3, held);
+        held = fetch_idx(tile + 4);               // before the K/V loads: never waits on them
         if (tile + 1 < ntiles) load_tile(tile + 1);
+        if (IDX) read_rows(tile + 2);
         if (tile <= wdiag) {
           f32x16 sacc[NSUB];
           qk(buf, sacc);
@@ -283,7 +363,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
           m = fmaxf(m, tile_max(sacc));
         }
         if (tile + 1 < ntiles) store_tile(buf ^ 1);
-        put_idx(tile + 2, inext);
         __syncthreads();
       }
       m_ref = m * c;
@@ -294,12 +373,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     begin_walk();
     for (int tile = 0; tile < ntiles; ++tile) {
       const int buf = tile & 1;
-      const int inext = fetch_idx(tile + 2);
+      put_idx(tile + 3, held);
+      held = fetch_idx(tile + 4);                 // before the K/V loads: never waits on them
       if (tile + 1 < ntiles) load_tile(tile + 1);
+      if (IDX) read_rows(tile + 2);
       if (tile < wdiag && tile > 0) {
-        f32x16 sacc[NSUB];              // hot path: no mask, no reductions
-        qk(buf, sacc);
-        pv(buf, sacc);
+        hot(buf);                       // no mask, no reductions
       } else if (tile <= wdiag) {
         f32x16 sacc[NSUB];
         qk(buf, sacc);
@@ -308,7 +387,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
         pv(buf, sacc);
       }
       if (tile + 1 < ntiles) store_tile(buf ^ 1);
-      put_idx(tile + 2, inext);
       __syncthreads();
     }
     const bool bad = !(sum_halves(l_run) <= kSumLimit);

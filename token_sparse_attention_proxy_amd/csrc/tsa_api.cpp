@@ -315,6 +315,17 @@ tsa_status tsa_attention_indexed(const tsa_problem* prob, const void* q, const v
                   "tsa_attention_indexed");
 }
 
+tsa_status tsa_zero_unselected(const tsa_problem* prob, const int32_t* rank, void* o,
+                               void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_problem(prob, &sh));
+  TSA_TRY(check_ptr(rank, "rank"));
+  TSA_TRY(check_ptr(o, "o"));
+  if (fault_injected()) return injected("tsa_zero_unselected");
+  return launched(tsa::launch_zero_unselected(sh, rank, o, hipStream_t(stream)),
+                  "tsa_zero_unselected");
+}
+
 tsa_status tsa_forward_fused(const tsa_problem* prob, const void* q, const void* k, const void* v,
                              void* o, int32_t* budget, int32_t* idx, void* ws, size_t ws_bytes,
                              void* stream) {

@@ -168,6 +168,14 @@ def tsa_attention_indexed(prob: Problem, q, k, v, idx, budget, o=None):
     return o
 
 
+def tsa_zero_unselected(prob: Problem, rank, o):
+    lib = _lib.load()
+    p = prob.c()
+    check(lib.tsa_zero_unselected(ctypes.byref(p), _ptr(rank), _ptr(o), _stream(o.device)),
+          "tsa_zero_unselected")
+    return o
+
+
 def tsa_forward_fused(prob: Problem, q, k, v, o=None, budget=None, idx=None, ws=None):
     lib = _lib.load()
     p = prob.c()
@@ -190,4 +198,4 @@ def forward(q, k, v, w: int, tau: float, fused: bool = False):
 __all__ = ["Problem", "TsaError", "workspace_bytes", "forward_workspace_bytes",
            "fused_workspace_bytes", "tsa_score", "tsa_budget", "tsa_select", "tsa_gather",
            "tsa_attention", "tsa_scatter", "tsa_forward", "tsa_attention_indexed",
-           "tsa_forward_fused", "forward"]
+           "tsa_forward_fused", "tsa_zero_unselected", "forward"]
