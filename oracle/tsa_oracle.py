@@ -38,6 +38,18 @@ design notes of the repository):
   * query head h reads K/V rows of KV head h // (Hq/Hkv) at its own indices;
   * each batch element is an independent sequence with its own budget.
 
+Alternative readings (ablations), each a keyword argument defaulting to the
+main reading above:
+  * ``causal=False`` in proxy_scores: every proxy row sees all L keys;
+  * ``per_head=True`` in coverage_budget: each head cuts its own importance
+    curve against tau, giving one budget K_h per (b, h) (a [B,Hq] array);
+  * ``keep=w`` in coverage_budget and select_heads: the last ``keep``
+    positions (the proxy window) are never pruned; only tokens before them
+    are candidates for pruning, and every head's set is its top-(K - keep)
+    candidates plus the window.
+Every function that takes a budget accepts either shape: [B] (one budget per
+sequence) or [B,Hq] (one per head).
+
 Pins (tests/test_oracle_pins.py) tie every function to closed forms, library
 routines, brute force and a hand-derived worked example.
 """
@@ -59,14 +71,21 @@ def _kv_head(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
+def head_budget(budget, b: int, h: int) -> int:
+    """K of head (b, h) from a [B] (per sequence) or [B,Hq] (per head) budget."""
+    budget = np.asarray(budget)
+    return int(budget[b, h]) if budget.ndim == 2 else int(budget[b])
+
+
 # ---------------------------------------------------------------------------
 # Step 1 [Scoring]: proxy attention of the last w queries against all keys,
 # softmax per row, column sums (divided by w) give per-token importance.
 # ---------------------------------------------------------------------------
-def proxy_scores(q, k, w: int) -> np.ndarray:
+def proxy_scores(q, k, w: int, causal: bool = True) -> np.ndarray:
     """Per-head token importance s[b,h,j] in float64.
 
     q: [B,Hq,L,d]; k: [B,Hkv,L,d]; returns [B,Hq,L] with each row summing to 1.
+    causal=False: every proxy row sees all L keys (alternative reading).
     """
     q = _f64(q)
     k = _f64(k)
@@ -75,7 +94,7 @@ def proxy_scores(q, k, w: int) -> np.ndarray:
     assert 1 <= w <= L and Hq % Hkv == 0
     rows = np.arange(L - w, L)
     cols = np.arange(L)
-    visible = cols[None, :] <= rows[:, None]          # causal proxy rows
+    visible = (cols[None, :] <= rows[:, None]) if causal else np.ones((w, L), dtype=bool)
     s = np.zeros((B, Hq, L))
     for b in range(B):
         for h in range(Hq):
@@ -124,31 +143,49 @@ def pruned_mass_curve(sigma_b) -> list:
     return c
 
 
-def coverage_budget(s, tau: float) -> np.ndarray:
-    """Budget K_b = L - P_b per batch element (int32 [B]).
+def _cut(masses, thr: int, pmax: int) -> int:
+    """P = max{p in [0, pmax] : C(p) <= thr}, C(p) = exact sum of the p smallest masses."""
+    c = pruned_mass_curve(masses)
+    p = 0
+    for pp in range(pmax + 1):       # C is non-decreasing: take the largest p with C(p) <= thr
+        if c[pp] <= thr:
+            p = pp
+        else:
+            break
+    return p
 
-    P_b = max{p in [0, L-1] : C(p) <= tau} with C measured as the head-mean
-    pruned mass; tau = 0 gives P_b = 0.
+
+def coverage_budget(s, tau: float, per_head: bool = False, keep: int = 0) -> np.ndarray:
+    """Budget K = L - P: int32 [B] (one per sequence) or, with per_head, [B,Hq].
+
+    Main reading: P_b = max{p in [0, L-1] : C(p) <= tau} with C measured as the
+    head-mean pruned mass; tau = 0 gives P_b = 0.
+    per_head: each head's own importance curve is cut against tau.
+    keep: the last ``keep`` positions are never pruned; candidates are the
+    first L - keep tokens and P = max{p in [0, min(L - keep, L - 1)] : C(p) <= tau}.
     """
     s = _f64(s)
     B, Hq, L = s.shape
+    assert 0 <= keep <= L
     tau32 = float(np.float32(tau))
     assert 0.0 <= tau32 < 1.0
-    out = np.zeros(B, dtype=np.int32)
+    ncand = L - keep
+    pmax = min(ncand, L - 1)
+    out = np.zeros((B, Hq) if per_head else B, dtype=np.int32)
     if tau32 == 0.0:
-        out[:] = L
+        out[...] = L
+        return out
+    if per_head:
+        thr = tau_threshold(tau32, 1)
+        qm = quantised_masses(s)
+        for b in range(B):
+            for h in range(Hq):
+                out[b, h] = L - _cut(qm[b, h, :ncand], thr, pmax)
         return out
     thr = tau_threshold(tau32, Hq)
     sig = head_sum_masses(s)
     for b in range(B):
-        c = pruned_mass_curve(sig[b])
-        p = 0
-        for pp in range(L):          # C is non-decreasing: take the largest p with C(p) <= thr
-            if c[pp] <= thr:
-                p = pp
-            else:
-                break
-        out[b] = L - p
+        out[b] = L - _cut(sig[b][:ncand], thr, pmax)
     return out
 
 
@@ -163,16 +200,22 @@ def select_topk(s_row, K: int):
     return np.sort(order[:K]).astype(np.int32)
 
 
-def select_heads(s, budget):
-    """idx [B,H,L] (ascending set then -1) and rank [B,H,L] (slot or -1)."""
+def select_heads(s, budget, keep: int = 0):
+    """idx [B,H,L] (ascending set then -1) and rank [B,H,L] (slot or -1).
+
+    keep: the last ``keep`` positions are always in the set; the other K - keep
+    come from the first L - keep tokens by (score desc, index asc).
+    """
     s = _f64(s)
     B, H, L = s.shape
     idx = np.full((B, H, L), -1, dtype=np.int32)
     rank = np.full((B, H, L), -1, dtype=np.int32)
+    window = np.arange(L - keep, L, dtype=np.int32)
     for b in range(B):
-        K = int(budget[b])
         for h in range(H):
-            sel = select_topk(s[b, h], K)
+            K = head_budget(budget, b, h)
+            assert keep <= K <= L
+            sel = np.concatenate([select_topk(s[b, h, :L - keep], K - keep), window])
             idx[b, h, :K] = sel
             rank[b, h, sel] = np.arange(K, dtype=np.int32)
     return idx, rank
@@ -191,8 +234,8 @@ def gather(q, k, v, idx, budget):
     kc = np.zeros((B, Hq, L, d))
     vc = np.zeros((B, Hq, L, d))
     for b in range(B):
-        K = int(budget[b])
         for h in range(Hq):
+            K = head_budget(budget, b, h)
             g = _kv_head(h, Hq, Hkv)
             sel = idx[b, h, :K]
             qc[b, h, :K] = q[b, h, sel]
@@ -234,8 +277,8 @@ def attention_heads(qc, kc, vc, budget) -> np.ndarray:
     B, H, L, d = qc.shape
     oc = np.zeros((B, H, L, d))
     for b in range(B):
-        K = int(budget[b])
         for h in range(H):
+            K = head_budget(budget, b, h)
             oc[b, h, :K] = causal_attention(qc[b, h, :K], kc[b, h, :K], vc[b, h, :K])
     return oc
 
@@ -262,8 +305,8 @@ def scatter(oc, idx, budget) -> np.ndarray:
     B, H, L, d = oc.shape
     o = np.zeros((B, H, L, d))
     for b in range(B):
-        K = int(budget[b])
         for h in range(H):
+            K = head_budget(budget, b, h)
             o[b, h, idx[b, h, :K]] = oc[b, h, :K]
     return o
 
@@ -271,10 +314,14 @@ def scatter(oc, idx, budget) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # The whole op: score -> budget -> per-head top-K -> gather -> attention -> scatter.
 # ---------------------------------------------------------------------------
-def forward(q, k, v, w: int, tau: float) -> dict:
-    s = proxy_scores(q, k, w)
-    budget = coverage_budget(s, tau)
-    idx, rank = select_heads(s, budget)
+def forward(q, k, v, w: int, tau: float, causal: bool = True, per_head: bool = False,
+            keep_window: bool = False) -> dict:
+    """The main reading by default; the keyword flags select the alternative
+    readings (keep_window keeps the w proxy positions)."""
+    keep = w if keep_window else 0
+    s = proxy_scores(q, k, w, causal=causal)
+    budget = coverage_budget(s, tau, per_head=per_head, keep=keep)
+    idx, rank = select_heads(s, budget, keep=keep)
     qc, kc, vc = gather(q, k, v, idx, budget)
     oc = attention_heads(qc, kc, vc, budget)
     o = scatter(oc, idx, budget)

@@ -340,6 +340,177 @@ def pin_forward_bruteforce(O):
             assert np.allclose(out["o"], o_bf, rtol=0, atol=1e-12), (trial, tau)
 
 
+# --------------------------------------------------------------------------- alternative readings
+def pin_worked_example_alternatives(O):
+    ex, q, k, v = load_worked_example()
+    alt = ex["alternatives"]
+    s = O.proxy_scores(q, k, ex["w"], causal=False)
+    want = np.array([_frac(x) for x in alt["noncausal_scores"]])
+    assert np.allclose(s[0, 0], want, rtol=0, atol=1e-14), (s, want)
+    for case in alt["noncausal_cases"]:
+        out = O.forward(q, k, v, ex["w"], case["tau"], causal=False)
+        assert int(out["budget"][0]) == case["budget"], (case, out["budget"])
+        assert list(out["idx"][0, 0, :case["budget"]]) == case["idx"]
+        want_o = np.array([_frac(x) for x in case["o"]])
+        assert np.allclose(out["o"][0, 0, :, 0], want_o, rtol=0, atol=1e-13), (case, out["o"])
+    for case in alt["keep_window_cases"]:
+        out = O.forward(q, k, v, ex["w"], case["tau"], keep_window=True)
+        assert int(out["budget"][0]) == case["budget"], (case, out["budget"])
+        assert list(out["idx"][0, 0, :case["budget"]]) == case["idx"]
+        want_o = np.array([_frac(x) for x in case["o"]])
+        assert np.allclose(out["o"][0, 0, :, 0], want_o, rtol=0, atol=1e-13), (case, out["o"])
+    # one head: the per-head budget is the global budget
+    for case in ex["cases"]:
+        out = O.forward(q, k, v, ex["w"], case["tau"], per_head=True)
+        assert out["budget"].shape == (1, 1) and int(out["budget"][0, 0]) == case["budget"]
+
+
+def pin_scores_noncausal(O):
+    """Every proxy row sees all L keys: identical keys give s_j = 1/L exactly; otherwise
+    s is the mean over the proxy rows of one library softmax over all keys."""
+    r = _rng(15)
+    for (L, w, d) in [(40, 8, 4), (12, 12, 2), (30, 1, 3)]:
+        k = np.tile(r.standard_normal(d), (L, 1)).reshape(1, 1, L, d)
+        q = r.standard_normal((1, 1, L, d)) * 3
+        s = O.proxy_scores(q, k, w, causal=False)[0, 0]
+        assert np.allclose(s, 1.0 / L, rtol=0, atol=1e-14), s
+    B, Hq, Hkv, L, d, w = 2, 4, 2, 23, 8, 5
+    q = r.standard_normal((B, Hq, L, d))
+    k = r.standard_normal((B, Hkv, L, d))
+    s = O.proxy_scores(q, k, w, causal=False)
+    kt = torch.from_numpy(k).repeat_interleave(Hq // Hkv, dim=1)
+    logits = torch.matmul(torch.from_numpy(q[:, :, L - w:]), kt.transpose(-1, -2).contiguous()) / math.sqrt(d)
+    want = torch.softmax(logits, dim=-1).mean(dim=2).numpy()
+    assert np.allclose(s, want, rtol=0, atol=1e-14)
+    # the causal reading differs (rows before the last see fewer keys) unless w = 1
+    assert not np.allclose(s, O.proxy_scores(q, k, w))
+    assert np.allclose(O.proxy_scores(q, k, 1, causal=False), O.proxy_scores(q, k, 1), rtol=0, atol=1e-15)
+
+
+def _bruteforce_cut(masses, t, pmax):
+    """max{p in [0, pmax] : min over p-subsets of the summed masses <= t} (exact fractions)."""
+    n = len(masses)
+    best = 0
+    for p in range(min(pmax, n) + 1):
+        cp = min(sum((masses[j] for j in sub), Fraction(0)) for sub in itertools.combinations(range(n), p))
+        if cp <= t:
+            best = p
+    return best
+
+
+def pin_budget_per_head_bruteforce(O):
+    r = _rng(23)
+    for trial in range(10):
+        B, H, L = 2, int(r.integers(1, 4)), int(r.integers(2, 9))
+        s = _dyadic_scores(r, B, H, L)
+        taus = [0.0, 0.01, 0.3, 0.999] + [float(np.sort(s[0, 0])[:p].sum()) for p in range(1, L)]
+        for tau in taus:
+            if not (0.0 <= float(np.float32(tau)) < 1.0):
+                continue
+            t = Fraction(float(np.float32(tau)))
+            kb = O.coverage_budget(s, tau, per_head=True)
+            assert kb.shape == (B, H)
+            for b in range(B):
+                for h in range(H):
+                    m = [Fraction(float(x)) for x in s[b, h]]
+                    want = L if t == 0 else L - _bruteforce_cut(m, t, L - 1)
+                    assert int(kb[b, h]) == want, (trial, b, h, tau, kb, want)
+            if H == 1:    # one head: the per-head cut is the global cut
+                assert np.array_equal(kb[:, 0], O.coverage_budget(s, tau))
+
+
+def pin_budget_keep_window_bruteforce(O):
+    r = _rng(24)
+    for trial in range(10):
+        B, H, L = 1, int(r.integers(1, 4)), int(r.integers(2, 9))
+        keep = int(r.integers(1, L + 1))
+        s = _dyadic_scores(r, B, H, L)
+        for tau in [0.0, 0.05, 0.2, 0.5, 0.9]:
+            t = Fraction(float(np.float32(tau)))
+            mean = [sum(Fraction(float(s[0, h, j])) for h in range(H)) / H for j in range(L)]
+            want = L if t == 0 else L - _bruteforce_cut(mean[:L - keep], t, L - keep)
+            kb = O.coverage_budget(s, tau, keep=keep)
+            assert int(kb[0]) == want, (trial, keep, tau, kb, want)
+            assert int(kb[0]) >= keep
+            kh = O.coverage_budget(s, tau, per_head=True, keep=keep)
+            for h in range(H):
+                m = [Fraction(float(x)) for x in s[0, h]]
+                wh = L if t == 0 else L - _bruteforce_cut(m[:L - keep], t, L - keep)
+                assert int(kh[0, h]) == wh, (trial, keep, tau, h, kh, wh)
+
+
+def pin_select_keep_window(O):
+    """With a kept window the set is the window plus the brute-force top of the rest."""
+    r = _rng(33)
+    for trial in range(8):
+        L = int(r.integers(2, 10))
+        keep = int(r.integers(1, L + 1))
+        s = (r.integers(0, 4, size=(1, 2, L)).astype(np.float64) / 8.0)
+        for K in range(keep, L + 1):
+            budget = np.full((1, 2), K, dtype=np.int32)           # per-head shape
+            idx, rank = O.select_heads(s, budget, keep=keep)
+            for h in range(2):
+                top = _bruteforce_select(list(s[0, h, :L - keep]), K - keep) if K > keep else []
+                want = sorted(top) + list(range(L - keep, L))
+                assert list(idx[0, h, :K]) == want, (trial, keep, K, h, idx[0, h])
+                assert np.all(idx[0, h, K:] == -1)
+                assert np.array_equal(rank[0, h, idx[0, h, :K]], np.arange(K))
+
+
+def _bruteforce_forward_alt(q, k, v, w, tau, causal, per_head, keep_window):
+    """Tiny-input pipeline for the alternative readings from library routines and enumeration."""
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    qt, kt, vt = (torch.from_numpy(x) for x in (q, k, v))
+    keep = w if keep_window else 0
+    t = Fraction(float(np.float32(tau)))
+    s = np.zeros((B, Hq, L))
+    for b in range(B):
+        for h in range(Hq):
+            for rr in range(L - w, L):
+                hi = L if not causal else rr + 1
+                x = (kt[b, h // G, :hi] @ qt[b, h, rr]) / math.sqrt(d)
+                s[b, h, :hi] += torch.softmax(x, 0).numpy() / w
+    o = np.zeros((B, Hq, L, d))
+    budgets = np.zeros((B, Hq), dtype=np.int64)
+    for b in range(B):
+        mean = [sum(Fraction(float(s[b, h, j])) for h in range(Hq)) / Hq for j in range(L)]
+        pmax = min(L - keep, L - 1)
+        Kg = L if t == 0 else L - _bruteforce_cut(mean[:L - keep], t, pmax)
+        for h in range(Hq):
+            if per_head:
+                m = [Fraction(float(x)) for x in s[b, h]]
+                K = L if t == 0 else L - _bruteforce_cut(m[:L - keep], t, pmax)
+            else:
+                K = Kg
+            budgets[b, h] = K
+            top = _bruteforce_select(list(s[b, h, :L - keep]), K - keep) if K > keep else []
+            sel = sorted(top) + list(range(L - keep, L))
+            ot = torch.nn.functional.scaled_dot_product_attention(
+                qt[b, h, sel][None], kt[b, h // G, sel][None], vt[b, h // G, sel][None],
+                is_causal=True)[0].numpy()
+            o[b, h, sel] = ot
+    return s, budgets, o
+
+
+def pin_forward_alternatives_bruteforce(O):
+    r = _rng(54)
+    for trial in range(8):
+        B, Hkv, G = 1, int(r.integers(1, 3)), int(r.integers(1, 3))
+        Hq, L, d = Hkv * G, int(r.integers(3, 8)), 2
+        w = int(r.integers(1, L + 1))
+        q, k, v = (r.standard_normal(sh) * 1.5 for sh in [(B, Hq, L, d), (B, Hkv, L, d), (B, Hkv, L, d)])
+        causal, per_head, keep_window = bool(trial & 1), bool(trial & 2), bool(trial & 4)
+        for tau in (0.0, 0.15, 0.4):
+            s_bf, kb_bf, o_bf = _bruteforce_forward_alt(q, k, v, w, tau, causal, per_head, keep_window)
+            out = O.forward(q, k, v, w, tau, causal=causal, per_head=per_head, keep_window=keep_window)
+            assert np.allclose(out["s"], s_bf, rtol=0, atol=1e-13)
+            got_b = out["budget"] if per_head else np.repeat(out["budget"][:, None], Hq, axis=1)
+            assert np.array_equal(got_b, kb_bf), (trial, tau, out["budget"], kb_bf)
+            assert np.allclose(out["o"], o_bf, rtol=0, atol=1e-12), (trial, tau)
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_scores_mass,
@@ -355,4 +526,10 @@ ALL_PINS = [
     pin_forward_tau0_dense,
     pin_forward_zero_rows_and_linearity,
     pin_forward_bruteforce,
+    pin_worked_example_alternatives,
+    pin_scores_noncausal,
+    pin_budget_per_head_bruteforce,
+    pin_budget_keep_window_bruteforce,
+    pin_select_keep_window,
+    pin_forward_alternatives_bruteforce,
 ]

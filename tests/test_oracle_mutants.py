@@ -25,7 +25,7 @@ def fresh_oracle():
 
 
 def _scores_variant(mask="causal", divide_w=True, scale=True, head_map="div", window="last"):
-    def proxy_scores(q, k, w):
+    def proxy_scores(q, k, w, causal=True):
         q = np.asarray(q, np.float64)
         k = np.asarray(k, np.float64)
         B, Hq, L, d = q.shape
@@ -33,7 +33,9 @@ def _scores_variant(mask="causal", divide_w=True, scale=True, head_map="div", wi
         G = Hq // Hkv
         rows = np.arange(L - w, L) if window == "last" else np.arange(w)
         cols = np.arange(L)
-        if mask == "causal":
+        if not causal:
+            vis = np.ones((len(rows), L), bool)
+        elif mask == "causal":
             vis = cols[None, :] <= rows[:, None]
         elif mask == "strict":
             vis = (cols[None, :] < rows[:, None]) | (cols[None, :] == 0)
@@ -86,8 +88,8 @@ def m_budget_strict(O):
 def m_budget_prune_crossing(O):
     orig = O.coverage_budget
 
-    def cb(s, tau):
-        kb = orig(s, tau)
+    def cb(s, tau, **kw):
+        kb = orig(s, tau, **kw)
         return np.maximum(kb - (1 if float(np.float32(tau)) > 0 else 0), 1).astype(np.int32)
     O.coverage_budget = cb
 
@@ -112,9 +114,9 @@ def m_budget_max_head(O):
 def m_budget_no_tau0(O):
     orig = O.coverage_budget
 
-    def cb(s, tau):
+    def cb(s, tau, **kw):
         s = np.asarray(s, np.float64)
-        if float(np.float32(tau)) == 0.0:
+        if float(np.float32(tau)) == 0.0 and not kw.get("per_head") and not kw.get("keep"):
             sig = O.head_sum_masses(s)
             out = []
             for b in range(s.shape[0]):
@@ -122,7 +124,7 @@ def m_budget_no_tau0(O):
                 p = max(pp for pp in range(s.shape[2]) if c[pp] <= 0)
                 out.append(s.shape[2] - p)
             return np.array(out, dtype=np.int32)
-        return orig(s, tau)
+        return orig(s, tau, **kw)
     O.coverage_budget = cb
 
 
@@ -206,11 +208,55 @@ def m_scatter_compact(O):
     O.scatter = scatter
 
 
+def m_noncausal_ignored(O):
+    orig = O.proxy_scores
+    O.proxy_scores = lambda q, k, w, causal=True: orig(q, k, w)
+
+
+def m_per_head_head_count_threshold(O):
+    orig_thr = O.tau_threshold
+    orig_cb = O.coverage_budget
+
+    def cb(s, tau, per_head=False, keep=0):
+        if not per_head:
+            return orig_cb(s, tau, per_head=per_head, keep=keep)
+        H = np.asarray(s).shape[1]
+        O.tau_threshold = lambda t, Hq: orig_thr(t, H)       # threshold of the head sum
+        try:
+            return orig_cb(s, tau, per_head=True, keep=keep)
+        finally:
+            O.tau_threshold = orig_thr
+    O.coverage_budget = cb
+
+
+def m_keep_ignored_in_budget(O):
+    orig = O.coverage_budget
+    O.coverage_budget = lambda s, tau, per_head=False, keep=0: orig(s, tau, per_head=per_head, keep=0)
+
+
+def m_keep_window_at_start(O):
+    def select_heads(s, budget, keep=0):
+        s = np.asarray(s, np.float64)
+        B, H, L = s.shape
+        idx = np.full((B, H, L), -1, dtype=np.int32)
+        rank = np.full((B, H, L), -1, dtype=np.int32)
+        for b in range(B):
+            for h in range(H):
+                K = O.head_budget(budget, b, h)
+                rest = O.select_topk(s[b, h, keep:], K - keep) + keep
+                sel = np.sort(np.concatenate([np.arange(keep), rest])).astype(np.int32)
+                idx[b, h, :K] = sel
+                rank[b, h, sel] = np.arange(K, dtype=np.int32)
+        return idx, rank
+    O.select_heads = select_heads
+
+
 MUTANTS = [m_no_causal, m_strict_causal, m_no_divide_w, m_no_scale, m_head_mod, m_first_rows,
            m_budget_strict, m_budget_prune_crossing, m_budget_descending, m_budget_max_head,
            m_budget_no_tau0, m_select_high_index_ties, m_select_unsorted,
            m_select_ascending_scores, m_attn_nomask, m_attn_strict, m_gather_wrong_kv,
-           m_scatter_compact]
+           m_scatter_compact, m_noncausal_ignored, m_per_head_head_count_threshold,
+           m_keep_ignored_in_budget, m_keep_window_at_start]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=[m.__name__ for m in MUTANTS])

@@ -297,8 +297,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     constexpr int NR = NQK + NPV;             // operand reads, in MFMA order
     constexpr int PF = 2;
     constexpr int LAST = NSUB - 1;
-    constexpr int LAST_SLOT = 2 * LAST * DT;  // PV MFMAs that carry the last subtile's softmax
-    static_assert(LAST >= 1 && 8 % KS == 0 && 8 % LAST_SLOT == 0, "pipeline shape");
+    constexpr int LAST_SLOT = 2 * LAST * DT;  // PV MFMAs that can carry the last subtile's softmax
+    constexpr int LPP = (8 + LAST_SLOT - 1) / LAST_SLOT;   // its pairs per carrying MFMA
+    static_assert(LAST >= 1 && 8 % KS == 0, "pipeline shape");
     const float mneg = -m_ref;
     const uint16_t* kbase = &sm.k[buf][krow][8 * half];
     const uint16_t* vbase = &sm.vt[buf][l32][8 * half];
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
                                                            oacc[dt], 0, 0, 0);
         if (j < LAST_SLOT) {
 #pragma unroll
-          for (int p = j * (8 / LAST_SLOT); p < (j + 1) * (8 / LAST_SLOT); ++p) softmax_pair(LAST, p);
+          for (int p = j * LPP; p < (j + 1) * LPP && p < 8; ++p) softmax_pair(LAST, p);
         }
       }
     }
