@@ -15,7 +15,9 @@ Printed as one JSON line, with:
   * a per-kernel breakdown of both paths timed with HIP events on the launch
     stream, and the roofline of the dominant kernel (the attention of the
     timed path) from those launches;
-  * the fp64 CPU oracle timed on a bounded sample of the same workload.
+  * the fp64 CPU oracle timed on a bounded sample of the same workload;
+  * the alternative readings (TSA_FLAG_* bits): K/L and ms per layer of the
+    timed path under each, against the same dense baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--path fused|steps]
@@ -23,6 +25,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -48,7 +51,11 @@ def log(*a):
 
 
 def attention_flops(budget, Hq: int, d: int) -> float:
-    """Algorithmic FLOPs of causal attention over K_b rows: 4d per visible (i, j) pair."""
+    """Algorithmic FLOPs of causal attention over K rows: 4d per visible (i, j) pair.
+    budget: [B] (every head of a sequence has K_b rows) or [B,Hq] (per head)."""
+    budget = np.asarray(budget)
+    if budget.ndim == 2:
+        return float(sum(2.0 * d * int(K) * (int(K) + 1) for K in budget.ravel()))
     return float(sum(2.0 * d * int(K) * (int(K) + 1) * Hq for K in budget))
 
 
@@ -127,6 +134,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--path", choices=["fused", "steps"], default="steps")
+    ap.add_argument("--no-readings", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -236,6 +244,42 @@ def main():
         del od
         log(f"[bench] dense attention {dense_ms:.3f} ms")
 
+    # ---- alternative readings: K/L and time of the whole op under each flag set
+    readings = None
+    if not args.no_readings:
+        readings = {}
+        NC, PH, KW = T.TSA_FLAG_NONCAUSAL_PROXY, T.TSA_FLAG_PER_HEAD_BUDGET, T.TSA_FLAG_KEEP_WINDOW
+        for name, fl in [("main", 0), ("noncausal_proxy", NC), ("per_head_budget", PH),
+                         ("keep_window", KW), ("all", NC | PH | KW)]:
+            p2 = dataclasses.replace(prob, flags=fl)
+            ws2 = torch.empty(T.forward_workspace_bytes(p2), dtype=torch.uint8, device=dev)
+            b2 = torch.empty(p2.budget_shape, dtype=torch.int32, device=dev)
+            fn = (lambda: T.tsa_forward_fused(p2, qd, kd, vd, o, b2, idx, ws2)) if args.path == "fused" \
+                else (lambda: T.tsa_forward(p2, qd, kd, vd, o, b2, idx, ws2))
+            fn()
+            torch.cuda.synchronize()
+            r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            rreps = max(2, min(args.steps, 3))
+            r0.record(st)
+            for _ in range(rreps):
+                fn()
+            r1.record(st)
+            torch.cuda.synchronize()
+            ms = r0.elapsed_time(r1) / rreps
+            kb = b2.cpu().numpy()
+            kl = kb.astype(np.float64) / wl.L
+            readings[name] = {"flags": fl, "ms_per_layer": round(ms, 4),
+                              "keep_frac_mean": round(float(kl.mean()), 5),
+                              "keep_frac_min": round(float(kl.min()), 5),
+                              "keep_frac_max": round(float(kl.max()), 5),
+                              "attention_tflop": round(attention_flops(kb, wl.Hq, wl.d) / 1e12, 3),
+                              "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms, 4)}
+            log(f"[bench] reading {name}: {ms:.3f} ms, K/L mean {kl.mean():.4f} "
+                f"[{kl.min():.4f}, {kl.max():.4f}]")
+            del ws2, b2
+        paths[args.path]()              # restore the main reading's budget, idx and o
+        torch.cuda.synchronize()
+
     # ---- roofline of the dominant kernel (the timed path's attention), algorithmic FLOPs
     bf16 = wl.dtype == "bf16"
     flops = attention_flops(bud, wl.Hq, wl.d)
@@ -307,6 +351,7 @@ def main():
         "path_kernels_ms": {p: {n: round(steps_ms[n], 4) for n in ks} for p, ks in path_kernels.items()},
         "kernels": kernels,
         "roofline": roofline,
+        "readings": readings,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

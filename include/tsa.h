@@ -61,13 +61,38 @@ typedef enum tsa_status {
 
 typedef enum tsa_dtype { TSA_F32 = 0, TSA_BF16 = 1 } tsa_dtype;
 
+/* Alternative readings of the method, as bits of tsa_problem.flags (0 = the
+ * main reading).  The pages leave these points open ("Dynamic Token
+ * Coverage", scoring and budget bullets); each bit switches one of them.
+ *   TSA_FLAG_NONCAUSAL_PROXY  every proxy row sees all L keys (main reading:
+ *                             row r sees keys j <= r).
+ *   TSA_FLAG_PER_HEAD_BUDGET  each head cuts its own importance curve
+ *                             against tau, so budgets differ per head: every
+ *                             `budget` argument is then [B,Hq] int32 instead
+ *                             of [B] (main reading: one budget per sequence
+ *                             from the head-mean importance).
+ *   TSA_FLAG_KEEP_WINDOW      the w proxy positions L-w..L-1 are never
+ *                             pruned: only tokens before them are pruning
+ *                             candidates, and every head keeps the window
+ *                             plus its top (K - w) candidates (K >= w). */
+enum {
+  TSA_FLAG_NONCAUSAL_PROXY = 1,
+  TSA_FLAG_PER_HEAD_BUDGET = 2,
+  TSA_FLAG_KEEP_WINDOW = 4
+};
+
 /* Problem shape.  w: number of proxy (most recent) queries; tau: coverage
- * threshold in [0, 1).  dtype: a tsa_dtype value. */
+ * threshold in [0, 1).  dtype: a tsa_dtype value.  flags: TSA_FLAG_* bits
+ * (0 for the main reading). */
 typedef struct tsa_problem {
   int32_t B, Hq, Hkv, L, d, w;
   float tau;
   int32_t dtype;
+  int32_t flags;
 } tsa_problem;
+
+/* "Budget" below means budget[b] for the main reading and budget[b,h] under
+ * TSA_FLAG_PER_HEAD_BUDGET; K_b (or K_bh) is that value. */
 
 /* Human-readable name of a status code (static storage). */
 const char* tsa_status_string(tsa_status st);

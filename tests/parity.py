@@ -80,46 +80,71 @@ def assert_outputs_close(o_gpu: np.ndarray, o_ref: np.ndarray, dtype: str, rows=
 
 
 def set_near_tie(s_ref_row: np.ndarray, sel_gpu, sel_ref, K: int) -> bool:
+    """K: the number of tokens chosen by score among ``s_ref_row`` (the candidates)."""
+    if K <= 0:
+        return set(map(int, sel_gpu)) == set(map(int, sel_ref))
     theta = np.sort(s_ref_row)[::-1][K - 1]
     diff = set(map(int, sel_gpu)) ^ set(map(int, sel_ref))
     return all(abs(s_ref_row[j] - theta) <= NEAR_TIE * theta for j in diff)
 
 
-def budget_near_tie(s_ref_b: np.ndarray, tau: float, K_gpu: int, K_ref: int) -> bool:
+def budget_near_tie(s_ref_b: np.ndarray, tau: float, K_gpu: int, K_ref: int, keep: int = 0) -> bool:
+    """s_ref_b: the [H, L] scores of one budget row (all heads of a sequence, or one head)."""
     Hq, L = s_ref_b.shape
-    sig = O.head_sum_masses(s_ref_b[None])[0]
+    sig = O.head_sum_masses(s_ref_b[None])[0][:L - keep]
     c = O.pruned_mass_curve(sig)
     scale = float(Hq) * float(2 ** O.SCORE_FRAC_BITS)
     p_lo, p_hi = sorted((L - K_gpu, L - K_ref))
-    return all(abs(c[p] / scale - tau) <= NEAR_TIE * tau for p in range(p_lo, p_hi + 2) if p <= L)
+    return all(abs(c[p] / scale - tau) <= NEAR_TIE * tau for p in range(p_lo, p_hi + 2)
+               if p < len(c))
+
+
+def _oracle_set(s_row: np.ndarray, K: int, keep: int) -> np.ndarray:
+    L = s_row.shape[0]
+    top = O.select_topk(s_row[:L - keep], K - keep) if K > keep else np.zeros(0, np.int32)
+    return np.concatenate([top, np.arange(L - keep, L)]).astype(np.int32)
 
 
 def compare_forward(ref: dict, o_gpu: np.ndarray, budget_gpu: np.ndarray, idx_gpu: np.ndarray,
-                    q, k, v, tau: float, dtype: str, sample_rows: int = 0, seed: int = 0):
+                    q, k, v, tau: float, dtype: str, sample_rows: int = 0, seed: int = 0,
+                    per_head: bool = False, keep: int = 0):
     """End-to-end comparison.  ``ref`` is the oracle's forward() dict (with "o"
     present unless sample_rows > 0, in which case outputs are recomputed for
-    sampled rows only).  Returns a report dict with near-tie counts."""
+    sampled rows only).  per_head / keep: the alternative readings (budgets
+    [B,Hq]; the last ``keep`` positions always kept).  Returns a report dict
+    with near-tie counts."""
     B, Hq, L = idx_gpu.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
     rep = {"budget_near_ties": 0, "set_near_ties": 0, "heads": B * Hq, "worst_err": 0.0}
     rng = np.random.default_rng(seed)
     for b in range(B):
-        Kg, Kr = int(budget_gpu[b]), int(ref["budget"][b])
-        if Kg != Kr:
-            assert budget_near_tie(ref["s"][b], tau, Kg, Kr), f"budget mismatch b={b}: {Kg} vs {Kr}"
-            rep["budget_near_ties"] += 1
+        if not per_head:
+            Kg, Kr = int(budget_gpu[b]), int(ref["budget"][b])
+            if Kg != Kr:
+                assert budget_near_tie(ref["s"][b], tau, Kg, Kr, keep), \
+                    f"budget mismatch b={b}: {Kg} vs {Kr}"
+                rep["budget_near_ties"] += 1
         for h in range(Hq):
+            if per_head:
+                Kg, Kr = int(budget_gpu[b, h]), int(ref["budget"][b, h])
+                if Kg != Kr:
+                    assert budget_near_tie(ref["s"][b, h][None], tau, Kg, Kr, keep), \
+                        f"budget mismatch b={b} h={h}: {Kg} vs {Kr}"
+                    rep["budget_near_ties"] += 1
+            assert Kg >= keep
             g = h // G
             sel_g = idx_gpu[b, h, :Kg]
             assert np.all(np.diff(sel_g) > 0) and np.all(idx_gpu[b, h, Kg:] == -1)
+            assert np.array_equal(sel_g[Kg - keep:], np.arange(L - keep, L))
             sel_r = ref["idx"][b, h, :Kr]
             same = Kg == Kr and np.array_equal(sel_g, sel_r)
             if not same:
-                # the GPU set must be the top-Kg set of the oracle scores up to near-ties
-                top_r = O.select_topk(ref["s"][b, h], Kg)
+                # the GPU set must be the oracle's set of size Kg up to near-ties
+                top_r = _oracle_set(ref["s"][b, h], Kg, keep)
                 if not np.array_equal(sel_g, top_r):
-                    assert set_near_tie(ref["s"][b, h], sel_g, top_r, Kg), f"set mismatch b={b} h={h}"
+                    assert set_near_tie(ref["s"][b, h, :L - keep], sel_g, top_r, Kg - keep), \
+                        f"set mismatch b={b} h={h}"
                 rep["set_near_ties"] += 1
             # unselected rows are exactly +0.0
             mask = np.ones(L, bool)

@@ -74,6 +74,15 @@ def test_workspace_sizes(lib):
     assert lib.tsa_fused_workspace_bytes(None) == 0
 
 
+def test_workspace_per_head_budget(lib):
+    """Per-head budgets need one mass row per head instead of one per sequence."""
+    g = lib.tsa_workspace_bytes(ctypes.byref(prob()))
+    ph = lib.tsa_workspace_bytes(ctypes.byref(prob(flags=_lib.TSA_FLAG_PER_HEAD_BUDGET)))
+    assert ph - g >= 8 * (8 - 1) * 1000 - 512     # up to alignment
+    for f in (_lib.TSA_FLAG_NONCAUSAL_PROXY, _lib.TSA_FLAG_KEEP_WINDOW):
+        assert lib.tsa_workspace_bytes(ctypes.byref(prob(flags=f))) == g
+
+
 def test_workspace_scales_with_headline_shape(lib):
     p = prob(Hq=32, Hkv=8, L=131072, w=64)
     fwd = lib.tsa_forward_workspace_bytes(ctypes.byref(p))
@@ -96,6 +105,8 @@ BAD_PROBLEMS = [
     (dict(d=256), _lib.TSA_ERR_UNSUPPORTED),
     (dict(dtype=7), _lib.TSA_ERR_UNSUPPORTED),
     (dict(Hq=64, Hkv=1, w=1000), _lib.TSA_ERR_UNSUPPORTED),
+    (dict(flags=8), _lib.TSA_ERR_UNSUPPORTED),
+    (dict(flags=-1), _lib.TSA_ERR_UNSUPPORTED),
 ]
 
 

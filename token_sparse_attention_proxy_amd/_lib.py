@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(PKG, "libtsa.so")
 
 TSA_OK, TSA_ERR_INVALID_ARG, TSA_ERR_UNSUPPORTED, TSA_ERR_WORKSPACE, TSA_ERR_HIP = range(5)
 TSA_F32, TSA_BF16 = 0, 1
+TSA_FLAG_NONCAUSAL_PROXY, TSA_FLAG_PER_HEAD_BUDGET, TSA_FLAG_KEEP_WINDOW = 1, 2, 4
 
 # Every symbol include/tsa.h declares.
 EXPORTS = ["tsa_status_string", "tsa_last_error", "tsa_version", "tsa_workspace_bytes",
@@ -24,7 +25,7 @@ EXPORTS = ["tsa_status_string", "tsa_last_error", "tsa_version", "tsa_workspace_
 class TsaProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("L", ctypes.c_int32), ("d", ctypes.c_int32), ("w", ctypes.c_int32),
-                ("tau", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("tau", ctypes.c_float), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 _P = ctypes.POINTER(TsaProblem)

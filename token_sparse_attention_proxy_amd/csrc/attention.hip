@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ budget,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ o, int Hq, int Hk, int kv_group,
-    int L, float c) {
+    int L, int bud_b, int bud_h, float c) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int KCH = kBN * D / 8 / kThreads;          // 16-byte K chunks per thread
   constexpr int VPAIRS = (kBN / 4) * (D / 8);          // (4-key group, 8-d chunk) pairs
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   const int bh = blockIdx.y;
   const int b = bh / Hq, h = bh % Hq;
   const int hk = h / kv_group;
-  const int n = budget ? min(max(budget[b], 0), L) : L;
+  const int n = budget ? min(max(budget[b * bud_b + h * bud_h], 0), L) : L;
   const int nqb = (L + kBM - 1) / kBM;
   const int q0 = (nqb - 1 - int(blockIdx.x)) * kBM;    // heaviest blocks first
   if (q0 >= n) return;
@@ -415,14 +415,14 @@ template <int D, bool IDX>
 __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ budget, const int32_t* __restrict__ idx, float* __restrict__ o,
-    int Hq, int Hk, int kv_group, int L, float c) {
+    int Hq, int Hk, int kv_group, int L, int bud_b, int bud_h, float c) {
   __shared__ float ks[kF32Keys][D];
   __shared__ float vs[kF32Keys][D];
   __shared__ int rows_s[kF32Keys];
   const int bh = blockIdx.y;
   const int b = bh / Hq, h = bh % Hq;
   const int hk = h / kv_group;
-  const int n = budget ? min(max(budget[b], 0), L) : L;
+  const int n = budget ? min(max(budget[b * bud_b + h * bud_h], 0), L) : L;
   const int nqb = (L + kF32Rows - 1) / kF32Rows;
   const int q0 = (nqb - 1 - int(blockIdx.x)) * kF32Rows;
   if (q0 >= n) return;
@@ -496,7 +496,7 @@ hipError_t run_bf16(const Shape& sh, const void* q, const void* k, const void* v
   attn_fwd_bf16<D, IDX><<<grid, kThreads, 0, st>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), budget, idx, static_cast<uint16_t*>(o), sh.Hq,
-      sh.Hq / kv_group, kv_group, sh.L, c);
+      sh.Hq / kv_group, kv_group, sh.L, sh.bud_b(), sh.bud_h(), c);
   return hipGetLastError();
 }
 
@@ -508,7 +508,8 @@ hipError_t run_f32(const Shape& sh, const void* q, const void* k, const void* v,
   dim3 grid((sh.L + kF32Rows - 1) / kF32Rows, sh.B * sh.Hq);
   attn_fwd_f32<D, IDX><<<grid, kF32Rows, 0, st>>>(
       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-      budget, idx, static_cast<float*>(o), sh.Hq, sh.Hq / kv_group, kv_group, sh.L, c);
+      budget, idx, static_cast<float*>(o), sh.Hq, sh.Hq / kv_group, kv_group, sh.L, sh.bud_b(),
+      sh.bud_h(), c);
   return hipGetLastError();
 }
 

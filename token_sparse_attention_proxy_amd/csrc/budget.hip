@@ -15,6 +15,11 @@
 // moves into the first digit bucket where the running mass exceeds thr.  It
 // stops when that bucket holds one value or all bits are fixed; all values
 // left in the bucket are then equal, and P follows in closed form.
+//
+// Alternative readings: with per-head budgets each (b, h) is a row of its
+// own (sigma = that head's quantised scores, thr = floor(tau*2^50)); with a
+// kept window only the first L - w tokens are candidates and
+// P = max{p in [0, min(L - w, L - 1)] : C(p) <= thr}.
 #include "tsa_device.h"
 #include "tsa_internal.h"
 
@@ -37,18 +42,19 @@ __global__ void clear_u64(uint64_t* __restrict__ p, int n) {
   if (i < n) p[i] = 0;
 }
 
-// sigma[b,j] = sum over query heads, in head order, of the quantised score.
+// sigma[r,j] = sum over the hpr query heads of budget row r, in head order,
+// of the quantised score, for the nc candidate tokens j < nc.
 __global__ __launch_bounds__(kSigmaThreads) void budget_sigma(const float* __restrict__ s,
                                                               uint64_t* __restrict__ sigma,
                                                               uint64_t* __restrict__ sigmax,
-                                                              int Hq, int L) {
+                                                              int hpr, int L, int nc) {
   __shared__ uint64_t red[kSigmaThreads / 64];
   const int b = blockIdx.y;
   const int j = blockIdx.x * kSigmaThreads + threadIdx.x;
   uint64_t acc = 0;
-  if (j < L) {
-    const float* sb = s + int64_t(b) * Hq * L + j;
-    for (int h = 0; h < Hq; ++h) acc += quantise(sb[int64_t(h) * L]);
+  if (j < nc) {
+    const float* sb = s + int64_t(b) * hpr * L + j;
+    for (int h = 0; h < hpr; ++h) acc += quantise(sb[int64_t(h) * L]);
     sigma[int64_t(b) * L + j] = acc;
   }
   // block max, then one integer atomic per block
@@ -67,11 +73,12 @@ __global__ __launch_bounds__(kSigmaThreads) void budget_sigma(const float* __res
   }
 }
 
-// One workgroup per sequence: radix descent for the coverage cut.
+// One workgroup per budget row: radix descent for the coverage cut over the
+// nc candidates; P is at most pmax.
 __global__ __launch_bounds__(kCutThreads) void budget_cut(const uint64_t* __restrict__ sigma,
                                                           const uint64_t* __restrict__ sigmax,
                                                           int32_t* __restrict__ budget, int L,
-                                                          uint64_t thr) {
+                                                          int nc, int pmax, uint64_t thr) {
   __shared__ uint32_t cnt[kBuckets];
   __shared__ uint64_t mass[kBuckets];
   __shared__ uint64_t scan_tmp[17];
@@ -100,7 +107,7 @@ __global__ __launch_bounds__(kCutThreads) void budget_cut(const uint64_t* __rest
     }
     if (t == 0) first_cross = kBuckets;
     __syncthreads();
-    for (int j = t; j < L; j += kCutThreads) {
+    for (int j = t; j < nc; j += kCutThreads) {
       const uint64_t v = sg[j];
       const uint64_t top = hi >= 64 ? 0 : (v >> hi);
       if (top == prefix) {
@@ -152,40 +159,45 @@ __global__ __launch_bounds__(kCutThreads) void budget_cut(const uint64_t* __rest
   if (t == 0) {
     uint64_t P;
     if (!crossed) {
-      P = uint64_t(L) - 1;
+      P = uint64_t(pmax);
     } else {
       const uint64_t m = (thr - mass_below) / T;
       P = cnt_below + (m < n_eq - 1 ? m : n_eq - 1);
-      if (P > uint64_t(L) - 1) P = uint64_t(L) - 1;
+      if (P > uint64_t(pmax)) P = uint64_t(pmax);
     }
     budget[b] = int32_t(uint64_t(L) - P);
   }
 }
 
-__global__ void budget_fill(int32_t* __restrict__ budget, int B, int L) {
+__global__ void budget_fill(int32_t* __restrict__ budget, int rows, int L) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < B) budget[i] = L;
+  if (i < rows) budget[i] = L;
 }
 
 }  // namespace
 
 hipError_t launch_budget(const Shape& sh, const float* scores, int32_t* budget, char* ws,
                          hipStream_t st) {
+  const int rows = sh.bud_rows();
   if (sh.tau == 0.0f) {   // tau = 0 prunes nothing
-    budget_fill<<<(sh.B + 255) / 256, 256, 0, st>>>(budget, sh.B, sh.L);
+    budget_fill<<<(rows + 255) / 256, 256, 0, st>>>(budget, rows, sh.L);
     return hipGetLastError();
   }
   const StepWs lay = step_ws_layout(sh);
   uint64_t* sigma = reinterpret_cast<uint64_t*>(ws + lay.sigma);
   uint64_t* sigmax = reinterpret_cast<uint64_t*>(ws + lay.sigmax);
-  // floor(Hq * tau * 2^50): tau has a 24-bit significand and Hq <= 2^12, so
+  const int hpr = sh.per_head() ? 1 : sh.Hq;     // query heads per budget row
+  const int nc = sh.L - sh.keep();                // pruning candidates
+  const int pmax = nc < sh.L - 1 ? nc : sh.L - 1;
+  // floor(hpr * tau * 2^50): tau has a 24-bit significand and hpr <= 2^12, so
   // the product is exact in double.
-  const double x = double(sh.Hq) * double(sh.tau) * 1125899906842624.0;
+  const double x = double(hpr) * double(sh.tau) * 1125899906842624.0;
   const uint64_t thr = uint64_t(x);
-  clear_u64<<<(sh.B + 255) / 256, 256, 0, st>>>(sigmax, sh.B);
-  budget_sigma<<<dim3((sh.L + kSigmaThreads - 1) / kSigmaThreads, sh.B), kSigmaThreads, 0, st>>>(
-      scores, sigma, sigmax, sh.Hq, sh.L);
-  budget_cut<<<sh.B, kCutThreads, 0, st>>>(sigma, sigmax, budget, sh.L, thr);
+  clear_u64<<<(rows + 255) / 256, 256, 0, st>>>(sigmax, rows);
+  if (nc > 0)
+    budget_sigma<<<dim3((nc + kSigmaThreads - 1) / kSigmaThreads, rows), kSigmaThreads, 0, st>>>(
+        scores, sigma, sigmax, hpr, sh.L, nc);
+  budget_cut<<<rows, kCutThreads, 0, st>>>(sigma, sigmax, budget, sh.L, nc, pmax, thr);
   return hipGetLastError();
 }
 

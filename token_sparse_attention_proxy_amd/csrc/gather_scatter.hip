@@ -28,19 +28,21 @@ template <int VPR>
 __global__ __launch_bounds__(kThreads) void gather_rows(
     const u32x4* __restrict__ q, const u32x4* __restrict__ k, const u32x4* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ budget, u32x4* __restrict__ qc,
-    u32x4* __restrict__ kc, u32x4* __restrict__ vc, int Hq, int Hkv, int L) {
+    u32x4* __restrict__ kc, u32x4* __restrict__ vc, int Hq, int Hkv, int L, int bud_b,
+    int bud_h) {
   constexpr int kRowsPerPass = kThreads / VPR;
   const int bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
   const int G = Hq / Hkv;
-  const int n = min(max(budget[b], 0), L);
   const int i0 = blockIdx.x * kRowsPerBlock;
-  if (i0 >= n) return;
   const int sub = threadIdx.x / VPR, vec = threadIdx.x % VPR;
   const int64_t grow = (int64_t(b) * Hkv + g) * L;        // first row of (b,g)
-  const int i1 = min(i0 + kRowsPerBlock, n);
   for (int hl = 0; hl < G; ++hl) {
-    const int64_t hrow = (int64_t(b) * Hq + g * G + hl) * L;   // first row of (b,h)
+    const int h = g * G + hl;
+    const int n = min(max(budget[b * bud_b + h * bud_h], 0), L);
+    if (i0 >= n) continue;
+    const int i1 = min(i0 + kRowsPerBlock, n);
+    const int64_t hrow = (int64_t(b) * Hq + h) * L;   // first row of (b,h)
     for (int i = i0 + sub; i < i1; i += kRowsPerPass) {
       const int src = idx[hrow + i];
       const int64_t dst = (hrow + i) * VPR + vec;
@@ -103,7 +105,7 @@ hipError_t gather_vpr(const Shape& sh, const void* q, const void* k, const void*
   gather_rows<VPR><<<grid, kThreads, 0, st>>>(
       static_cast<const u32x4*>(q), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
       idx, budget, static_cast<u32x4*>(qc), static_cast<u32x4*>(kc), static_cast<u32x4*>(vc),
-      sh.Hq, sh.Hkv, sh.L);
+      sh.Hq, sh.Hkv, sh.L, sh.bud_b(), sh.bud_h());
   return hipGetLastError();
 }
 

@@ -21,6 +21,8 @@
 // halves, then the row tiles of the head (through LDS, in tile order).  The Q
 // fragments and the LDS K reads are identical in the two orientations.
 // f32 path: plain fp32 VALU kernels (one key per thread).
+//
+// causal = 0 (alternative reading): every proxy row sees all L keys.
 #include <type_traits>
 
 #include "tsa_device.h"
@@ -62,7 +64,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void score_pass1(const T* __restrict__ q,
                                                         const T* __restrict__ k,
                                                         float2* __restrict__ part, int Hq, int Hkv,
-                                                        int L, int w, int n_chunk, float c) {
+                                                        int L, int w, int n_chunk, float c,
+                                                        int causal) {
   __shared__ float qs[kRowTile * D];
   __shared__ float red[2][kRowTile][kThreads / 64];
   const int chunk = blockIdx.x;
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void score_pass1(const T* __restrict__ q,
     __syncthreads();
     for (int ri = 0; ri < n; ++ri) {
       const int r = L - w + r0 + ri;
-      const bool vis = j <= r;   // causal proxy row; also excludes j >= L
+      const bool vis = causal ? j <= r : j < L;   // j <= r also excludes j >= L
       const float x = vis ? dot_scaled<D>(kr, qs + ri * D, c) : -INFINITY;
       const float m = wave_max(x);
       const float e = vis ? exp2f(x - m) : 0.f;
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void score_pass2(const T* __restrict__ q,
                                                         const T* __restrict__ k,
                                                         const float2* __restrict__ rowstat,
                                                         float* __restrict__ s, int Hq, int Hkv,
-                                                        int L, int w, float c) {
+                                                        int L, int w, float c, int causal) {
   __shared__ float qs[kRowTile * D];
   __shared__ float2 st[kRowTile];
   const int chunk = blockIdx.x;
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void score_pass2(const T* __restrict__ q,
     __syncthreads();
     for (int ri = 0; ri < n; ++ri) {
       const int r = L - w + r0 + ri;
-      if (j <= r) {
+      if (causal ? j <= r : j < L) {
         const float x = dot_scaled<D>(kr, qs + ri * D, c);
         acc += exp2f(x - st[ri].x) * st[ri].y;
       }
@@ -221,7 +224,7 @@ __device__ __forceinline__ float xhalf_other(float x) {
 template <int D>
 __global__ __launch_bounds__(kMThreads) void score_mfma_rowstats(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, float2* __restrict__ part,
-    int Hq, int Hkv, int L, int w, int n_chunk, float c) {
+    int Hq, int Hkv, int L, int w, int n_chunk, float c, int causal) {
   constexpr int KS = D / 16;
   __shared__ uint16_t ks[kScoreChunk][D + kMPad];
   const int chunk = blockIdx.x, bg = blockIdx.y;
@@ -232,8 +235,9 @@ __global__ __launch_bounds__(kMThreads) void score_mfma_rowstats(
   const int l32 = lane & 31, half = lane >> 5;
   stage_k_chunk<D>(k + (int64_t(b) * Hkv + g) * L * D, L, j0, ks);
   __syncthreads();
-  // keys of this chunk that some proxy row cannot see: masking needed
-  const bool edge = j0 + kScoreChunk - 1 > L - w;
+  // keys of this chunk that some proxy row cannot see (causal), or keys past
+  // L (either reading): masking needed
+  const bool edge = causal ? j0 + kScoreChunk - 1 > L - w : j0 + kScoreChunk > L;
   const f32x16 zero = {};
   for (int unit = wave; unit < G * RT; unit += kMThreads / 64) {
     const int h = g * G + unit / RT, r0 = 32 * (unit % RT);
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(kMThreads) void score_mfma_rowstats(
       for (int e = 0; e < 16; ++e) {
         const int key = j0 + 32 * kt + 8 * (e >> 2) + 4 * half + (e & 3);
         x[e] = acc[e] * c;
-        if (edge && (key > pos || r >= w)) x[e] = -INFINITY;
+        if (edge && (key > (causal ? pos : L - 1) || r >= w)) x[e] = -INFINITY;
         tm = fmaxf(tm, x[e]);
       }
       const float mn = fmaxf(m, tm);
@@ -284,7 +288,7 @@ template <int D>
 __global__ __launch_bounds__(kMThreads) void score_mfma_colsum(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const float2* __restrict__ rowstat, float* __restrict__ s, int Hq, int Hkv, int L, int w,
-    float c) {
+    float c, int causal) {
   constexpr int KS = D / 16;
   extern __shared__ float colsum[];       // [G*RT][kScoreChunk]
   __shared__ uint16_t ks[kScoreChunk][D + kMPad];
@@ -296,7 +300,9 @@ __global__ __launch_bounds__(kMThreads) void score_mfma_colsum(
   const int l32 = lane & 31, half = lane >> 5;
   stage_k_chunk<D>(k + (int64_t(b) * Hkv + g) * L * D, L, j0, ks);
   __syncthreads();
-  const bool edge = j0 + kScoreChunk - 1 > L - w;
+  // causal: keys of this chunk that some proxy row cannot see.  Keys past L
+  // never reach s, so the non-causal reading needs no mask here.
+  const bool edge = causal && j0 + kScoreChunk - 1 > L - w;
   const f32x16 zero = {};
   for (int unit = wave; unit < G * RT; unit += kMThreads / 64) {
     const int h = g * G + unit / RT, r0 = 32 * (unit % RT);
@@ -361,20 +367,22 @@ hipError_t run(const Shape& sh, const void* q, const void* k, float* scores, cha
     const size_t colsum_bytes = sizeof(float) * size_t(units) * kScoreChunk;
     score_mfma_rowstats<D><<<grid, kMThreads, 0, st>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), part, sh.Hq, sh.Hkv,
-        sh.L, sh.w, nc, c);
+        sh.L, sh.w, nc, c, int(sh.causal_proxy()));
     score_merge<<<unsigned((rows + kMergeWaves - 1) / kMergeWaves), 64 * kMergeWaves, 0, st>>>(
         part, rowstat, rows, nc);
     score_mfma_colsum<D><<<grid, kMThreads, colsum_bytes, st>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), rowstat, scores, sh.Hq,
-        sh.Hkv, sh.L, sh.w, c);
+        sh.Hkv, sh.L, sh.w, c, int(sh.causal_proxy()));
   } else {
     const dim3 grid(nc, sh.B * sh.Hq);
     score_pass1<T, D><<<grid, kThreads, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
-                                                 part, sh.Hq, sh.Hkv, sh.L, sh.w, nc, c);
+                                                 part, sh.Hq, sh.Hkv, sh.L, sh.w, nc, c,
+                                                 int(sh.causal_proxy()));
     score_merge<<<unsigned((rows + kMergeWaves - 1) / kMergeWaves), 64 * kMergeWaves, 0, st>>>(
         part, rowstat, rows, nc);
     score_pass2<T, D><<<grid, kThreads, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
-                                                 rowstat, scores, sh.Hq, sh.Hkv, sh.L, sh.w, c);
+                                                 rowstat, scores, sh.Hq, sh.Hkv, sh.L, sh.w, c,
+                                                 int(sh.causal_proxy()));
   }
   return hipGetLastError();
 }

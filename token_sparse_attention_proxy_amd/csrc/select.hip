@@ -14,6 +14,10 @@
 //      (greater, equal) counts gives every kept token its output slot.
 // Only integer operations are involved: results are bit-exact and
 // deterministic.
+//
+// Kept window (alternative reading): the last `keep` positions are always
+// in the set; the radix selection then runs over the first L - keep tokens
+// with K - keep slots, and the window fills slots K - keep .. K - 1.
 #include "tsa_device.h"
 #include "tsa_internal.h"
 
@@ -31,15 +35,17 @@ __global__ __launch_bounds__(kThreads) void select_topk(const float* __restrict_
                                                         const int32_t* __restrict__ budget,
                                                         int32_t* __restrict__ idx,
                                                         int32_t* __restrict__ rank, int Hq,
-                                                        int L) {
+                                                        int L, int bud_b, int bud_h, int keep) {
   __shared__ uint32_t hist[kBuckets];
   __shared__ uint64_t scan_tmp[17];
   __shared__ int dsel;
   __shared__ uint32_t sh_above;
   const int bh = blockIdx.x;
-  const int b = bh / Hq;
+  const int b = bh / Hq, h = bh % Hq;
   const int t = threadIdx.x;
-  const int K = min(max(budget[b], 0), L);
+  const int K = min(max(budget[b * bud_b + h * bud_h], 0), L);
+  const int nc = L - keep;                      // candidates: tokens before the kept window
+  const int Kc = max(K - keep, 0);              // slots filled by selection
   const float* sh = s + int64_t(bh) * L;
   int32_t* ih = idx + int64_t(bh) * L;
   int32_t* rh = rank + int64_t(bh) * L;
@@ -55,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void select_topk(const float* __restrict_
     for (int i = t; i < kBuckets; i += kThreads) hist[i] = 0;
     if (t == 0) dsel = -1;
     __syncthreads();
-    for (int j = t; j < L; j += kThreads) {
+    for (int j = t; j < nc; j += kThreads) {
       const uint32_t u = score_key(sh[j]);
       const uint32_t top = hi >= 32 ? 0u : (u >> hi);
       if (top == prefix) atomicAdd(&hist[(u >> lo) & ((1u << width) - 1u)], 1u);
@@ -67,8 +73,8 @@ __global__ __launch_bounds__(kThreads) void select_topk(const float* __restrict_
     uint64_t tot;
     const uint64_t excl = block_excl_scan_u64(uint64_t(cA) + cB, scan_tmp, &tot);
     // largest digit whose cumulative count from the top reaches K
-    if (uint64_t(above) + excl + cA >= uint64_t(K)) atomicMax(&dsel, dA);
-    else if (uint64_t(above) + excl + cA + cB >= uint64_t(K)) atomicMax(&dsel, dB);
+    if (uint64_t(above) + excl + cA >= uint64_t(Kc)) atomicMax(&dsel, dA);
+    else if (uint64_t(above) + excl + cA + cB >= uint64_t(Kc)) atomicMax(&dsel, dB);
     __syncthreads();
     const int d = dsel < 0 ? 0 : dsel;
     if (t == ((kBuckets - 1 - d) >> 1)) sh_above = above + uint32_t(excl) + ((d == dB) ? cA : 0u);
@@ -78,14 +84,14 @@ __global__ __launch_bounds__(kThreads) void select_topk(const float* __restrict_
     __syncthreads();
   }
   const uint32_t T = prefix;
-  const uint32_t need = uint32_t(K) - above;   // T-valued tokens to keep, lowest indices first
+  const uint32_t need = uint32_t(Kc) - above;  // T-valued tokens to keep, lowest indices first
 
   // ---- 2. ascending compaction
   uint32_t carry_gt = 0, carry_eq = 0;
-  for (int base = 0; base < L; base += kThreads) {
+  for (int base = 0; base < nc; base += kThreads) {
     const int j = base + t;
     uint32_t gt = 0, eq = 0;
-    if (j < L) {
+    if (j < nc) {
       const uint32_t u = score_key(sh[j]);
       gt = u > T;
       eq = u == T;
@@ -94,9 +100,9 @@ __global__ __launch_bounds__(kThreads) void select_topk(const float* __restrict_
     const uint64_t ex = block_excl_scan_u64((uint64_t(gt) << 32) | eq, scan_tmp, &tot);
     const uint32_t gt_before = carry_gt + uint32_t(ex >> 32);
     const uint32_t eq_before = carry_eq + uint32_t(ex & 0xffffffffu);
-    if (j < L) {
-      const bool keep = gt || (eq && eq_before < need);
-      if (keep) {
+    if (j < nc) {
+      const bool kept = gt || (eq && eq_before < need);
+      if (kept) {
         const uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
         ih[pos] = j;
         rh[j] = int32_t(pos);
@@ -107,7 +113,13 @@ __global__ __launch_bounds__(kThreads) void select_topk(const float* __restrict_
     carry_gt += uint32_t(tot >> 32);
     carry_eq += uint32_t(tot & 0xffffffffu);
   }
-  for (int i = K + t; i < L; i += kThreads) ih[i] = -1;
+  // the kept window, in order after the selected candidates
+  for (int j = nc + t; j < L; j += kThreads) {
+    const int pos = Kc + (j - nc);
+    ih[pos] = j;
+    rh[j] = pos;
+  }
+  for (int i = Kc + keep + t; i < L; i += kThreads) ih[i] = -1;
 }
 
 }  // namespace
@@ -115,7 +127,8 @@ __global__ __launch_bounds__(kThreads) void select_topk(const float* __restrict_
 hipError_t launch_select(const Shape& sh, const float* scores, const int32_t* budget,
                          int32_t* idx, int32_t* rank, char* ws, hipStream_t st) {
   (void)ws;
-  select_topk<<<sh.B * sh.Hq, kThreads, 0, st>>>(scores, budget, idx, rank, sh.Hq, sh.L);
+  select_topk<<<sh.B * sh.Hq, kThreads, 0, st>>>(scores, budget, idx, rank, sh.Hq, sh.L,
+                                                 sh.bud_b(), sh.bud_h(), sh.keep());
   return hipGetLastError();
 }
 

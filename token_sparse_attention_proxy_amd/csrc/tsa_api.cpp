@@ -47,6 +47,8 @@ tsa_status check_problem(const tsa_problem* p, tsa::Shape* out) {
   if (int64_t(p->L) > tsa::kMaxL) return fail(TSA_ERR_INVALID_ARG, "L=%d exceeds 2^22", p->L);
   if (std::isnan(p->tau) || !(p->tau >= 0.0f) || !(p->tau < 1.0f))
     return fail(TSA_ERR_INVALID_ARG, "tau=%g is outside [0, 1)", double(p->tau));
+  if (p->flags & ~(TSA_FLAG_NONCAUSAL_PROXY | TSA_FLAG_PER_HEAD_BUDGET | TSA_FLAG_KEEP_WINDOW))
+    return fail(TSA_ERR_UNSUPPORTED, "unknown flag bits 0x%x", unsigned(p->flags));
   if (p->dtype != TSA_F32 && p->dtype != TSA_BF16)
     return fail(TSA_ERR_UNSUPPORTED, "dtype %d is not supported (TSA_F32=0, TSA_BF16=1)", p->dtype);
   if (p->d != 64 && p->d != 128)
@@ -55,7 +57,7 @@ tsa_status check_problem(const tsa_problem* p, tsa::Shape* out) {
     return fail(TSA_ERR_UNSUPPORTED,
                 "(Hq/Hkv) * ceil(w/32) = %d proxy-row tiles per KV head exceeds %d",
                 (p->Hq / p->Hkv) * ((p->w + 31) / 32), tsa::kMaxScoreTiles);
-  *out = tsa::Shape{p->B, p->Hq, p->Hkv, p->L, p->d, p->w, p->tau, p->dtype};
+  *out = tsa::Shape{p->B, p->Hq, p->Hkv, p->L, p->d, p->w, p->tau, p->dtype, p->flags};
   return TSA_OK;
 }
 
@@ -106,9 +108,9 @@ StepWs step_ws_layout(const Shape& s) {
   w.rowstat = off;
   off = align256(off + sizeof(float) * 2 * size_t(s.B) * s.Hq * s.w);
   w.sigma = off;
-  off = align256(off + sizeof(uint64_t) * size_t(s.B) * s.L);
+  off = align256(off + sizeof(uint64_t) * size_t(s.bud_rows()) * s.L);
   w.sigmax = off;
-  off = align256(off + sizeof(uint64_t) * size_t(s.B));
+  off = align256(off + sizeof(uint64_t) * size_t(s.bud_rows()));
   w.selstate = off;
   off = align256(off + sizeof(int32_t) * 4 * size_t(s.B) * s.Hq);
   w.total = off;

@@ -21,7 +21,15 @@ struct Shape {
   int B, Hq, Hkv, L, d, w;
   float tau;
   int dtype;          // TSA_F32 / TSA_BF16
+  int flags;          // TSA_FLAG_* bits
   int G() const { return Hq / Hkv; }
+  bool causal_proxy() const { return !(flags & TSA_FLAG_NONCAUSAL_PROXY); }
+  bool per_head() const { return (flags & TSA_FLAG_PER_HEAD_BUDGET) != 0; }
+  int keep() const { return (flags & TSA_FLAG_KEEP_WINDOW) ? w : 0; }
+  // Budget of head (b, h) is budget[b * bud_b() + h * bud_h()].
+  int bud_b() const { return per_head() ? Hq : 1; }
+  int bud_h() const { return per_head() ? 1 : 0; }
+  int bud_rows() const { return per_head() ? B * Hq : B; }
   int eb() const { return dtype == TSA_BF16 ? 2 : 4; }
   int64_t row_bytes() const { return int64_t(d) * eb(); }
   int n_chunk() const { return (L + kScoreChunk - 1) / kScoreChunk; }
@@ -31,8 +39,8 @@ struct Shape {
 struct StepWs {
   size_t part;        // float2 [B*Hq*w*n_chunk]: per-chunk (max, sum) of each proxy row
   size_t rowstat;     // float2 [B*Hq*w]: (max in exp2 units, 1/Z) of each proxy row
-  size_t sigma;       // uint64 [B*L]: head-summed quantised masses
-  size_t sigmax;      // uint64 [B]: max sigma per sequence
+  size_t sigma;       // uint64 [R*L]: quantised masses (R = budget rows; head-summed if R = B)
+  size_t sigmax;      // uint64 [R]: max sigma per budget row
   size_t selstate;    // int32 [B*Hq*4]: per-head selection threshold state
   size_t total;
 };

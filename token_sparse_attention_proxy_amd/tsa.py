@@ -12,7 +12,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import TSA_BF16, TSA_F32, TsaError, TsaProblem, check
+from ._lib import (TSA_BF16, TSA_F32, TSA_FLAG_KEEP_WINDOW, TSA_FLAG_NONCAUSAL_PROXY,
+                   TSA_FLAG_PER_HEAD_BUDGET, TsaError, TsaProblem, check)
 
 _DTYPES = {"f32": (TSA_F32, torch.float32), "bf16": (TSA_BF16, torch.bfloat16)}
 
@@ -27,14 +28,16 @@ class Problem:
     w: int
     tau: float
     dtype: str = "bf16"          # "f32" or "bf16"
+    flags: int = 0               # TSA_FLAG_* bits (alternative readings)
 
     @classmethod
-    def from_qkv(cls, q: torch.Tensor, k: torch.Tensor, w: int, tau: float) -> "Problem":
+    def from_qkv(cls, q: torch.Tensor, k: torch.Tensor, w: int, tau: float,
+                 flags: int = 0) -> "Problem":
         B, Hq, L, d = q.shape
         dt = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(q.dtype)
         if dt is None:
             raise TypeError(f"unsupported dtype {q.dtype}")
-        return cls(B, Hq, k.shape[1], L, d, w, float(tau), dt)
+        return cls(B, Hq, k.shape[1], L, d, w, float(tau), dt, int(flags))
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -42,7 +45,13 @@ class Problem:
 
     def c(self) -> TsaProblem:
         code = _DTYPES[self.dtype][0] if self.dtype in _DTYPES else 99
-        return TsaProblem(self.B, self.Hq, self.Hkv, self.L, self.d, self.w, self.tau, code)
+        return TsaProblem(self.B, self.Hq, self.Hkv, self.L, self.d, self.w, self.tau, code,
+                          self.flags)
+
+    @property
+    def budget_shape(self) -> tuple:
+        """[B], or [B,Hq] with per-head budgets."""
+        return (self.B, self.Hq) if self.flags & TSA_FLAG_PER_HEAD_BUDGET else (self.B,)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -96,7 +105,7 @@ def tsa_budget(prob: Problem, s, budget=None, ws=None):
     lib = _lib.load()
     p = prob.c()
     if budget is None:
-        budget = _empty((prob.B,), torch.int32, s)
+        budget = _empty(prob.budget_shape, torch.int32, s)
     ws = _ws(prob, s, ws, workspace_bytes(prob))
     check(lib.tsa_budget(ctypes.byref(p), _ptr(s), _ptr(budget), _ptr(ws), ws.numel(),
                          _stream(s.device)), "tsa_budget")
@@ -149,7 +158,7 @@ def tsa_forward(prob: Problem, q, k, v, o=None, budget=None, idx=None, ws=None):
     lib = _lib.load()
     p = prob.c()
     o = _empty(q.shape, q.dtype, q) if o is None else o
-    budget = _empty((prob.B,), torch.int32, q) if budget is None else budget
+    budget = _empty(prob.budget_shape, torch.int32, q) if budget is None else budget
     idx = _empty((prob.B, prob.Hq, prob.L), torch.int32, q) if idx is None else idx
     ws = _ws(prob, q, ws, forward_workspace_bytes(prob))
     check(lib.tsa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(budget),
@@ -180,7 +189,7 @@ def tsa_forward_fused(prob: Problem, q, k, v, o=None, budget=None, idx=None, ws=
     lib = _lib.load()
     p = prob.c()
     o = _empty(q.shape, q.dtype, q) if o is None else o
-    budget = _empty((prob.B,), torch.int32, q) if budget is None else budget
+    budget = _empty(prob.budget_shape, torch.int32, q) if budget is None else budget
     idx = _empty((prob.B, prob.Hq, prob.L), torch.int32, q) if idx is None else idx
     ws = _ws(prob, q, ws, fused_workspace_bytes(prob))
     check(lib.tsa_forward_fused(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
@@ -189,13 +198,14 @@ def tsa_forward_fused(prob: Problem, q, k, v, o=None, budget=None, idx=None, ws=
     return o, budget, idx
 
 
-def forward(q, k, v, w: int, tau: float, fused: bool = False):
+def forward(q, k, v, w: int, tau: float, fused: bool = False, flags: int = 0):
     """The whole op on torch device tensors: returns (o, budget, idx)."""
-    prob = Problem.from_qkv(q, k, w, tau)
+    prob = Problem.from_qkv(q, k, w, tau, flags)
     return (tsa_forward_fused if fused else tsa_forward)(prob, q, k, v)
 
 
 __all__ = ["Problem", "TsaError", "workspace_bytes", "forward_workspace_bytes",
            "fused_workspace_bytes", "tsa_score", "tsa_budget", "tsa_select", "tsa_gather",
            "tsa_attention", "tsa_scatter", "tsa_forward", "tsa_attention_indexed",
-           "tsa_forward_fused", "tsa_zero_unselected", "forward"]
+           "tsa_forward_fused", "tsa_zero_unselected", "forward", "TSA_FLAG_NONCAUSAL_PROXY",
+           "TSA_FLAG_PER_HEAD_BUDGET", "TSA_FLAG_KEEP_WINDOW"]
