@@ -50,6 +50,13 @@ main reading above:
 Every function that takes a budget accepts either shape: [B] (one budget per
 sequence) or [B,Hq] (one per head).
 
+Composition with block-sparse attention on the compressed tensors (the pages
+name it as compatible, without fixing a format): ``block_sparse_attention``
+restricts the causal attention of the compact rows to the (query block, key
+block) pairs a caller marks visible, in blocks of ``BLOCK`` = 64 compact rows;
+the diagonal block of every query block is always visible, so no row is left
+without keys.
+
 Pins (tests/test_oracle_pins.py) tie every function to closed forms, library
 routines, brute force and a hand-derived worked example.
 """
@@ -61,6 +68,7 @@ from fractions import Fraction
 import numpy as np
 
 SCORE_FRAC_BITS = 50   # importance masses are counted in units of 2^-50
+BLOCK = 64             # rows per block of the block-sparse composition
 
 
 def _f64(x):
@@ -269,6 +277,38 @@ def causal_attention(qc, kc, vc, rows=None, block: int = 256) -> np.ndarray:
         p = np.exp(x)
         out[a:a + block] = (p @ vc[:hi]) / p.sum(axis=1, keepdims=True)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Composition [Compression]: block-sparse attention on the compressed tensors.
+# ---------------------------------------------------------------------------
+def block_sparse_attention(qc, kc, vc, block_mask, rows=None) -> np.ndarray:
+    """O_i = sum over visible j of softmax_j(Qc_i . Kc_j / sqrt(d)) Vc_j for one head.
+
+    Key j is visible to row i when j <= i and either i and j lie in the same
+    block of BLOCK rows or block_mask[i // BLOCK, j // BLOCK] is true.
+    block_mask: bool array with at least ceil(n / BLOCK) rows and columns.
+    """
+    qc, kc, vc = _f64(qc), _f64(kc), _f64(vc)
+    n, d = qc.shape
+    bm = np.asarray(block_mask, dtype=bool)
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((rows.shape[0], d))
+    scale = 1.0 / math.sqrt(d)
+    for a, i in enumerate(rows):
+        j = np.arange(i + 1)
+        vis = (j // BLOCK == i // BLOCK) | bm[i // BLOCK, j // BLOCK]
+        x = (kc[j[vis]] @ qc[i]) * scale
+        p = np.exp(x - x.max())
+        out[a] = (p @ vc[j[vis]]) / p.sum()
+    return out
+
+
+def unpack_block_mask(words, nb: int) -> np.ndarray:
+    """[nb, ceil(nb/32)] uint32 words -> [nb, nb] bool: bit kb % 32 of word kb // 32."""
+    words = np.asarray(words, dtype=np.uint64)
+    kb = np.arange(nb)
+    return ((words[:, kb // 32] >> (kb % 32).astype(np.uint64)) & 1).astype(bool)
 
 
 def attention_heads(qc, kc, vc, budget) -> np.ndarray:

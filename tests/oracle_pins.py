@@ -511,6 +511,56 @@ def pin_forward_alternatives_bruteforce(O):
             assert np.allclose(out["o"], o_bf, rtol=0, atol=1e-12), (trial, tau)
 
 
+# --------------------------------------------------------------------------- block-sparse composition
+def pin_block_sparse_closed_forms(O):
+    """Q = 0 gives uniform weights: row i's output is the mean of V over exactly the
+    keys it may see, which pins the mask rule (block indices, orientation, the
+    always-visible diagonal block) independently of the softmax."""
+    r = _rng(44)
+    Bk = O.BLOCK
+    n, d = 3 * Bk, 4
+    kc, vc = r.standard_normal((n, d)), r.standard_normal((n, d))
+    qz = np.zeros((n, d))
+    bm = np.zeros((3, 3), bool)
+    bm[2, 0] = True                                  # block 2 also sees block 0; nothing else
+    got = O.block_sparse_attention(qz, kc, vc, bm)
+    for i in range(n):
+        ib = i // Bk
+        keys = list(range(ib * Bk, i + 1))
+        if ib == 2:
+            keys = list(range(0, Bk)) + keys
+        assert np.allclose(got[i], vc[keys].mean(axis=0), rtol=0, atol=1e-13), i
+    # all-false: every block attends only within itself = per-block causal attention (library)
+    qc = r.standard_normal((n + 17, d))
+    kc2, vc2 = r.standard_normal((n + 17, d)), r.standard_normal((n + 17, d))
+    got = O.block_sparse_attention(qc, kc2, vc2, np.zeros((4, 4), bool))
+    for b0 in range(0, n + 17, Bk):
+        sl = slice(b0, min(b0 + Bk, n + 17))
+        want = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(qc[sl])[None], torch.from_numpy(kc2[sl])[None],
+            torch.from_numpy(vc2[sl])[None], is_causal=True)[0].numpy()
+        assert np.allclose(got[sl], want, rtol=0, atol=1e-12)
+    # all-true: plain causal attention (library)
+    got = O.block_sparse_attention(qc, kc2, vc2, np.ones((4, 4), bool))
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qc)[None], torch.from_numpy(kc2)[None], torch.from_numpy(vc2)[None],
+        is_causal=True)[0].numpy()
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+    rows = np.array([0, 70, n + 16])
+    assert np.allclose(O.block_sparse_attention(qc, kc2, vc2, np.ones((4, 4), bool), rows=rows),
+                       want[rows], rtol=0, atol=1e-12)
+
+
+def pin_block_mask_bits(O):
+    """Word w of row qb holds key blocks 32w .. 32w+31, bit kb % 32 (least significant first)."""
+    words = np.array([[0b101, 0], [1 << 31, 1], [0, 0]], dtype=np.uint32)   # nb = 35: 2 words per row
+    m = O.unpack_block_mask(words, 35)
+    assert m.shape == (3, 35)
+    assert list(np.nonzero(m[0])[0]) == [0, 2]
+    assert list(np.nonzero(m[1])[0]) == [31, 32]
+    assert not m[2].any()
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_scores_mass,
@@ -532,4 +582,6 @@ ALL_PINS = [
     pin_budget_keep_window_bruteforce,
     pin_select_keep_window,
     pin_forward_alternatives_bruteforce,
+    pin_block_sparse_closed_forms,
+    pin_block_mask_bits,
 ]

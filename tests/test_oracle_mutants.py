@@ -251,12 +251,59 @@ def m_keep_window_at_start(O):
     O.select_heads = select_heads
 
 
+def _bsa_variant(kind):
+    def block_sparse_attention(qc, kc, vc, block_mask, rows=None):
+        qc, kc, vc = (np.asarray(x, np.float64) for x in (qc, kc, vc))
+        n, d = qc.shape
+        bm = np.asarray(block_mask, bool)
+        Bk = O_BLOCK
+        rows = np.arange(n) if rows is None else np.asarray(rows)
+        out = np.empty((len(rows), d))
+        for a, i in enumerate(rows):
+            j = np.arange(i + 1)
+            if kind == "transposed":
+                vis = (j // Bk == i // Bk) | bm[j // Bk, i // Bk]
+            elif kind == "no_diagonal":
+                vis = bm[i // Bk, j // Bk] | (j == i)
+            else:                                     # block index off by one row
+                vis = (j // Bk == i // Bk) | bm[(i + 1) // Bk % bm.shape[0], j // Bk]
+            x = kc[j[vis]] @ qc[i] / math.sqrt(d)
+            p = np.exp(x - x.max())
+            out[a] = p @ vc[j[vis]] / p.sum()
+        return out
+    return block_sparse_attention
+
+
+O_BLOCK = 64
+
+
+def m_bsa_transposed(O):
+    O.block_sparse_attention = _bsa_variant("transposed")
+
+
+def m_bsa_no_diagonal(O):
+    O.block_sparse_attention = _bsa_variant("no_diagonal")
+
+
+def m_bsa_off_by_one(O):
+    O.block_sparse_attention = _bsa_variant("off_by_one")
+
+
+def m_mask_bits_msb_first(O):
+    def unpack(words, nb):
+        words = np.asarray(words, dtype=np.uint64)
+        kb = np.arange(nb)
+        return ((words[:, kb // 32] >> (31 - kb % 32).astype(np.uint64)) & 1).astype(bool)
+    O.unpack_block_mask = unpack
+
+
 MUTANTS = [m_no_causal, m_strict_causal, m_no_divide_w, m_no_scale, m_head_mod, m_first_rows,
            m_budget_strict, m_budget_prune_crossing, m_budget_descending, m_budget_max_head,
            m_budget_no_tau0, m_select_high_index_ties, m_select_unsorted,
            m_select_ascending_scores, m_attn_nomask, m_attn_strict, m_gather_wrong_kv,
            m_scatter_compact, m_noncausal_ignored, m_per_head_head_count_threshold,
-           m_keep_ignored_in_budget, m_keep_window_at_start]
+           m_keep_ignored_in_budget, m_keep_window_at_start, m_bsa_transposed, m_bsa_no_diagonal,
+           m_bsa_off_by_one, m_mask_bits_msb_first]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=[m.__name__ for m in MUTANTS])
