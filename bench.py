@@ -17,7 +17,10 @@ Printed as one JSON line, with:
     timed path) from those launches;
   * the fp64 CPU oracle timed on a bounded sample of the same workload;
   * the alternative readings (TSA_FLAG_* bits): K/L and ms per layer of the
-    timed path under each, against the same dense baseline.
+    timed path under each, against the same dense baseline;
+  * the block-sparse composition: the attention on the compressed tensors
+    under seeded block masks of several densities (ms, visible fraction,
+    TFLOP/s on the visible block pairs).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--path fused|steps]
@@ -57,6 +60,20 @@ def attention_flops(budget, Hq: int, d: int) -> float:
     if budget.ndim == 2:
         return float(sum(2.0 * d * int(K) * (int(K) + 1) for K in budget.ravel()))
     return float(sum(2.0 * d * int(K) * (int(K) + 1) * Hq for K in budget))
+
+
+def block_sparse_flops(words: np.ndarray, n: int, d: int) -> float:
+    """Algorithmic FLOPs (4d per visible causal pair) of block-sparse attention over the
+    first n compact rows of every head: visible off-diagonal blocks plus the diagonal."""
+    B, H, nb, nw = words.shape
+    bits = np.unpackbits(words.view(np.uint8).reshape(B, H, nb, nw * 4), axis=-1,
+                         bitorder="little")[..., :nb].astype(bool)
+    size = np.minimum(64, np.maximum(0, n - 64 * np.arange(nb)))          # rows per block
+    below = np.tril(np.ones((nb, nb), dtype=bool), k=-1)
+    pairs_off = (bits & below) * (size[:, None] * size[None, :])
+    pairs_diag = size * (size + 1) // 2
+    total = pairs_off.sum(axis=(-2, -1)).astype(np.float64) + pairs_diag.sum()
+    return float(4.0 * d * total.sum())
 
 
 def source_hash(path: str) -> str:
@@ -135,6 +152,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--path", choices=["fused", "steps"], default="steps")
     ap.add_argument("--no-readings", action="store_true")
+    ap.add_argument("--no-block-sparse", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -280,6 +298,36 @@ def main():
         paths[args.path]()              # restore the main reading's budget, idx and o
         torch.cuda.synchronize()
 
+    # ---- block-sparse composition on the compressed tensors of this step
+    block_sparse = None
+    if not args.no_block_sparse and wl.B == 1:
+        block_sparse = {}
+        n = int(bud[0])
+        for name, pat, dens in [("all", "all", 1.0), ("random_0.5", "random", 0.5),
+                                ("random_0.25", "random", 0.25), ("random_0.1", "random", 0.1),
+                                ("vertical_slash", "vertical_slash", 0.0)]:
+            mw = inputs.make_block_mask(wl.B, wl.Hq, wl.L, seed=1234, pattern=pat, density=dens,
+                                        band=16, columns=32)
+            md = torch.from_numpy(mw.view(np.int32)).to(dev)
+            T.tsa_attention_block_sparse(prob, qc, kc, vc, md, budget, 1, oc)
+            torch.cuda.synchronize()
+            b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            breps = max(2, min(args.steps, 3))
+            b0.record(st)
+            for _ in range(breps):
+                T.tsa_attention_block_sparse(prob, qc, kc, vc, md, budget, 1, oc)
+            b1.record(st)
+            torch.cuda.synchronize()
+            ms = b0.elapsed_time(b1) / breps
+            fl = block_sparse_flops(mw, n, wl.d)
+            block_sparse[name] = {"ms": round(ms, 4), "visible_frac": round(fl / attention_flops(bud, wl.Hq, wl.d), 4),
+                                  "TFLOP_s": round(fl / (ms * 1e-3) / 1e12, 2),
+                                  "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+                                  if wl.dtype == "bf16" else None}
+            log(f"[bench] block-sparse {name}: {ms:.3f} ms, visible {block_sparse[name]['visible_frac']:.3f}, "
+                f"{block_sparse[name]['TFLOP_s']} TFLOP/s")
+            del md
+
     # ---- roofline of the dominant kernel (the timed path's attention), algorithmic FLOPs
     bf16 = wl.dtype == "bf16"
     flops = attention_flops(bud, wl.Hq, wl.d)
@@ -352,6 +400,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "readings": readings,
+        "block_sparse": block_sparse,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -164,6 +164,27 @@ tsa_status tsa_gather(const tsa_problem* prob, const void* q, const void* k, con
 tsa_status tsa_attention(const tsa_problem* prob, const void* q, const void* k, const void* v,
                          const int32_t* budget, int32_t kv_group, void* o, void* stream);
 
+/* Words of the block mask taken by tsa_attention_block_sparse:
+ * B * Hq * NB * NW with NB = ceil(L/64), NW = ceil(NB/32).  0 on an invalid
+ * problem. */
+size_t tsa_block_mask_words(const tsa_problem* prob);
+
+/* Block-sparse attention on the compressed tensors: the composition with
+ * sparse attention kernels that the pages name (section 3 "Key
+ * contributions", compatibility item; section 4, combination with
+ * FlexPrefill).  The sparse pattern itself comes from the caller.  As
+ * tsa_attention, except that key j is visible to row i only when j <= i and
+ * either i and j lie in the same block of 64 rows, or the mask marks the
+ * (i / 64, j / 64) block pair visible:
+ *   block_mask[((b*Hq + h)*NB + qb)*NW + kb/32] bit (kb % 32) == 1.
+ * Diagonal blocks are always visible (so every row keeps at least itself);
+ * bits at or above the diagonal are ignored.  Masked tiles are neither
+ * loaded nor computed.  block_mask: device uint32, tsa_block_mask_words
+ * words.  Results equal tsa_attention when every bit is set. */
+tsa_status tsa_attention_block_sparse(const tsa_problem* prob, const void* q, const void* k,
+                                      const void* v, const int32_t* budget, int32_t kv_group,
+                                      const uint32_t* block_mask, void* o, void* stream);
+
 /* Decompression ("Core architecture", stage 2).  For every j < L:
  *   o[b,h,j] = rank[b,h,j] >= 0 ? oc[b,h,rank[b,h,j]] : +0.0
  * Each output row is written exactly once.  oc: [B,Hq,L,d]; rank: [B,Hq,L]

@@ -74,6 +74,14 @@ def test_workspace_sizes(lib):
     assert lib.tsa_fused_workspace_bytes(None) == 0
 
 
+def test_block_mask_words(lib):
+    # L=1000: 16 blocks of 64, one word per mask row
+    assert lib.tsa_block_mask_words(ctypes.byref(prob())) == 1 * 8 * 16 * 1
+    # L=131072: 2048 blocks, 64 words per row
+    assert lib.tsa_block_mask_words(ctypes.byref(prob(Hq=32, Hkv=8, L=131072))) == 32 * 2048 * 64
+    assert lib.tsa_block_mask_words(ctypes.byref(prob(Hkv=3))) == 0
+
+
 def test_workspace_per_head_budget(lib):
     """Per-head budgets need one mass row per head instead of one per sequence."""
     g = lib.tsa_workspace_bytes(ctypes.byref(prob()))
@@ -124,6 +132,8 @@ def _call_all(lib, p, ptr=FAKE, ws_bytes=1 << 40, kv_group=1):
         "forward_fused": lib.tsa_forward_fused(P, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ws_bytes,
                                                None),
         "zero_unselected": lib.tsa_zero_unselected(P, ptr, ptr, None),
+        "attention_block_sparse": lib.tsa_attention_block_sparse(P, ptr, ptr, ptr, ptr, kv_group,
+                                                                 ptr, ptr, None),
     }
 
 

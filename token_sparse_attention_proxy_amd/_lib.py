@@ -19,7 +19,8 @@ TSA_FLAG_NONCAUSAL_PROXY, TSA_FLAG_PER_HEAD_BUDGET, TSA_FLAG_KEEP_WINDOW = 1, 2,
 EXPORTS = ["tsa_status_string", "tsa_last_error", "tsa_version", "tsa_workspace_bytes",
            "tsa_forward_workspace_bytes", "tsa_score", "tsa_budget", "tsa_select", "tsa_gather",
            "tsa_attention", "tsa_scatter", "tsa_forward", "tsa_fused_workspace_bytes",
-           "tsa_attention_indexed", "tsa_forward_fused", "tsa_zero_unselected"]
+           "tsa_attention_indexed", "tsa_forward_fused", "tsa_zero_unselected",
+           "tsa_block_mask_words", "tsa_attention_block_sparse"]
 
 
 class TsaProblem(ctypes.Structure):
@@ -50,6 +51,8 @@ _SIGNATURES = {
     "tsa_attention_indexed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tsa_forward_fused": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "tsa_zero_unselected": (ctypes.c_int, [_P, _vp, _vp, _vp]),
+    "tsa_block_mask_words": (_sz, [_P]),
+    "tsa_attention_block_sparse": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
 }
 
 _lib = None

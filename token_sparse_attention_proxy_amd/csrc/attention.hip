@@ -33,7 +33,12 @@
 //     rows: out-of-range rows read as 0 and are never written, without
 //     branches;
 //   * only each wave's diagonal tile is masked; tiles above it are skipped;
-//   * query blocks are issued heaviest first (the causal triangle).
+//   * query blocks are issued heaviest first (the causal triangle);
+//   * block-sparse composition (BS): a caller's bit mask over (64-row query
+//     block, 64-key block) pairs of the compressed sequence says which key
+//     tiles each query block sees (its diagonal block always).  A workgroup
+//     stages only the tiles some of its four query blocks see, and each wave
+//     computes only the tiles its own query block sees.
 // f32 path: a plain fp32 VALU kernel (one query row per thread).
 #include "tsa_device.h"
 #include "tsa_internal.h"
@@ -89,12 +94,16 @@ __device__ __forceinline__ int acc_key(int e, int half) {
 // IDX = true: compact row i of head (b,h) is sequence row idx[b,h,i]; Q, K, V
 // are read and O is written through the index set (compression, attention
 // and decompression of the selected rows in one pass).
-template <int D, bool IDX>
+// BS = true: bmask is the block mask, [B*Hq][NB][NW] uint32 with NB = ceil(L/64)
+// and NW = ceil(NB/32); bit kb % 32 of word [qb][kb / 32] set = query block qb
+// sees key block kb.
+template <int D, bool IDX, bool BS>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ budget,
-    const int32_t* __restrict__ idx, uint16_t* __restrict__ o, int Hq, int Hk, int kv_group,
-    int L, int bud_b, int bud_h, float c) {
+    const int32_t* __restrict__ idx, const uint32_t* __restrict__ bmask,
+    uint16_t* __restrict__ o, int Hq, int Hk, int kv_group, int L, int bud_b, int bud_h,
+    float c) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int KCH = kBN * D / 8 / kThreads;          // 16-byte K chunks per thread
   constexpr int VPAIRS = (kBN / 4) * (D / 8);          // (4-key group, 8-d chunk) pairs
@@ -344,10 +353,172 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
       }
     }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    // Pin the operand reads PF MFMAs ahead, whatever the surrounding code.
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int i = 0; i < NR - PF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+  };
+
+  // Block mask of this head (BS only).  The workgroup's query blocks are
+  // qb0 .. qb0 + QB - 1; each wave's query block is its diagonal tile.  The
+  // walk keeps a cursor on one 32-tile word of the mask: the four rows' words
+  // of the current word are in registers and those of the next word are
+  // prefetched, so finding the next tile and whether a wave uses it is
+  // register arithmetic; only a run of empty words costs a wait.  Mask words
+  // are read with buffer (vector-memory) loads, which never share a wait
+  // counter with the LDS operand reads of the MFMA loop.
+  constexpr int QB = kBM / kBN;
+  const int NB = (L + kBN - 1) / kBN, NW = (NB + 31) >> 5;
+  const __amdgpu_buffer_rsrc_t rmask =
+      make_rsrc(BS ? bmask + int64_t(bh) * NB * NW : bmask, BS ? uint32_t(NB * NW) * 4 : 0u);
+  const int qb0 = q0 / kBN;
+  const int wsel = wdiag - qb0;          // this wave's row among the QB (0 .. QB-1)
+  int wd_cur = 0;                        // word under the cursor
+  uint32_t rw_cur[QB], rw_nxt[QB];       // row words of word wd_cur and wd_cur + 1
+  auto load_word = [&](int wd, uint32_t (&rw)[QB]) {   // rows past NB read as 0 (outside the buffer)
+    const bool in = wd < NW;
+#pragma unroll
+    for (int i = 0; i < QB; ++i)
+      rw[i] = uint32_t(__builtin_amdgcn_raw_buffer_load_b32(rmask, ((qb0 + i) * NW + (in ? wd : 0)) * 4, 0, 0));
+    if (!in) {
+#pragma unroll
+      for (int i = 0; i < QB; ++i) rw[i] = 0u;
+    }
+  };
+  // Tiles of word wd the workgroup needs: mask bits of its rows below qb0,
+  // every tile in [qb0, ntiles) (diagonal blocks), nothing at or past ntiles.
+  auto needed_bits = [&](int wd, const uint32_t (&rw)[QB]) {
+    uint32_t u = 0;
+#pragma unroll
+    for (int i = 0; i < QB; ++i) u |= rw[i];
+    const int lo = wd << 5;
+    const int a = min(max(qb0 - lo, 0), 32), e = min(max(ntiles - lo, 0), 32);
+    const uint32_t below_e = e >= 32 ? ~0u : ((1u << e) - 1u);
+    const uint32_t from_a = a >= 32 ? 0u : (~0u << a);
+    u = (u & ~from_a) | from_a;          // tiles >= qb0 are always needed
+    return __builtin_amdgcn_readfirstlane(u & below_e);
+  };
+  auto next_from = [&](int p) {          // first needed tile >= p; moves the cursor to it
+    if ((p >> 5) == wd_cur) {
+      const uint32_t u = needed_bits(wd_cur, rw_cur) & (~0u << (p & 31));
+      if (u) return (wd_cur << 5) + __builtin_ctz(u);
+      p = (wd_cur + 1) << 5;
+    }
+    if ((p >> 5) == wd_cur + 1 && p < ntiles) {   // step onto the prefetched word
+      ++wd_cur;
+#pragma unroll
+      for (int i = 0; i < QB; ++i) rw_cur[i] = rw_nxt[i];
+      load_word(wd_cur + 1, rw_nxt);
+      const uint32_t u = needed_bits(wd_cur, rw_cur) & (~0u << (p & 31));
+      if (u) return (wd_cur << 5) + __builtin_ctz(u);
+      p = (wd_cur + 1) << 5;
+    }
+    while (p < ntiles) {                 // a run of empty words: load as we go
+      wd_cur = p >> 5;
+      load_word(wd_cur, rw_cur);
+      load_word(wd_cur + 1, rw_nxt);
+      const uint32_t u = needed_bits(wd_cur, rw_cur) & (~0u << (p & 31));
+      if (u) return (wd_cur << 5) + __builtin_ctz(u);
+      p = (wd_cur + 1) << 5;
+    }
+    return ntiles;
+  };
+  auto wave_uses = [&](int t) {          // needs the cursor on t's word
+    if (t > wdiag) return false;
+    if (t == wdiag || !BS) return true;
+    if (wdiag >= NB) return false;       // a wave past the last row
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < QB; ++i) w = (i == wsel) ? rw_cur[i] : w;
+    return ((__builtin_amdgcn_readfirstlane(w) >> (t & 31)) & 1u) != 0;
+  };
+  auto begin_bs = [&]() {                // cursor on word 0; returns the first tile
+    wd_cur = 0;
+    load_word(0, rw_cur);
+    load_word(1, rw_nxt);
+    return next_from(0);
   };
 
   // attempt 0: reference = max of the first key tile; attempt 1 (rare): exact row max.
   for (int attempt = 0; attempt < 2; ++attempt) {
+    if constexpr (BS) {
+      // Walk only the tiles the workgroup needs, double-buffered in order.
+      // The next tile, and whether this wave uses it, are looked up one
+      // iteration ahead, so no mask read sits in front of a tile's work.
+      if (attempt == 1) {
+        float m = -INFINITY;
+        int cur = begin_bs(), buf = 0;
+        bool use_cur = wave_uses(cur);
+        int nxt = next_from(cur + 1);
+        bool use_nxt = nxt < ntiles && wave_uses(nxt);
+        load_tile(cur);
+        store_tile(0);
+        __syncthreads();
+        while (true) {
+          const int nxt2 = nxt < ntiles ? next_from(nxt + 1) : ntiles;   // before the K/V loads
+          const bool use_nxt2 = nxt2 < ntiles && wave_uses(nxt2);
+          if (nxt < ntiles) load_tile(nxt);
+          if (use_cur) {
+            f32x16 sacc[NSUB];
+            qk(buf, sacc);
+            if (cur == wdiag) mask(cur * kBN, sacc);
+            m = fmaxf(m, tile_max(sacc));
+          }
+          if (nxt < ntiles) store_tile(buf ^ 1);
+          __syncthreads();
+          if (nxt >= ntiles) break;
+          cur = nxt;
+          nxt = nxt2;
+          use_cur = use_nxt;
+          use_nxt = use_nxt2;
+          buf ^= 1;
+        }
+        m_ref = m * c;
+      }
+#pragma unroll
+      for (int i = 0; i < DT; ++i) oacc[i] = zero;
+      l_run = 0.f;
+      bool have_ref = attempt == 1;      // the first tile a wave uses sets its reference
+      int cur = begin_bs(), buf = 0;
+      bool use_cur = wave_uses(cur);
+      int nxt = next_from(cur + 1);
+      bool use_nxt = nxt < ntiles && wave_uses(nxt);
+      load_tile(cur);
+      store_tile(0);
+      __syncthreads();
+      while (true) {
+        const int nxt2 = nxt < ntiles ? next_from(nxt + 1) : ntiles;     // before the K/V loads
+        const bool use_nxt2 = nxt2 < ntiles && wave_uses(nxt2);
+        if (nxt < ntiles) load_tile(nxt);
+        if (use_cur) {
+          if (cur < wdiag && have_ref) {
+            hot(buf);
+          } else {
+            f32x16 sacc[NSUB];
+            qk(buf, sacc);
+            if (cur == wdiag) mask(cur * kBN, sacc);
+            if (!have_ref) m_ref = tile_max(sacc) * c;
+            pv(buf, sacc);
+          }
+          have_ref = true;
+        }
+        if (nxt < ntiles) store_tile(buf ^ 1);
+        __syncthreads();
+        if (nxt >= ntiles) break;
+        cur = nxt;
+        nxt = nxt2;
+        use_cur = use_nxt;
+        use_nxt = use_nxt2;
+        buf ^= 1;
+      }
+      const bool bad = !(sum_halves(l_run) <= kSumLimit);
+      if (!__syncthreads_or(bad)) break;
+      continue;
+    }
     if (attempt == 1) {
       float m = -INFINITY;
       begin_walk();
@@ -411,11 +582,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
 constexpr int kF32Rows = 64;    // query rows per workgroup (one per thread)
 constexpr int kF32Keys = 32;    // keys per LDS tile
 
-template <int D, bool IDX>
+template <int D, bool IDX, bool BS>
 __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const int32_t* __restrict__ budget, const int32_t* __restrict__ idx, float* __restrict__ o,
-    int Hq, int Hk, int kv_group, int L, int bud_b, int bud_h, float c) {
+    const int32_t* __restrict__ budget, const int32_t* __restrict__ idx,
+    const uint32_t* __restrict__ bmask, float* __restrict__ o, int Hq, int Hk, int kv_group,
+    int L, int bud_b, int bud_h, float c) {
+  static_assert(kF32Rows == 64 && 64 % kF32Keys == 0, "block mask granularity");
   __shared__ float ks[kF32Keys][D];
   __shared__ float vs[kF32Keys][D];
   __shared__ int rows_s[kF32Keys];
@@ -441,7 +614,11 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32(
   }
   float m = -INFINITY, l = 0.f;
   const int kv_end = min(q0 + kF32Rows, n);
+  const int NB = (L + 63) / 64, NW = (NB + 31) >> 5, qb = q0 / 64;
+  const uint32_t* __restrict__ bm_row = BS ? bmask + (int64_t(bh) * NB + qb) * NW : nullptr;
   for (int key0 = 0; key0 < kv_end; key0 += kF32Keys) {
+    const int kb = key0 / 64;
+    if (BS && kb != qb && !((bm_row[kb >> 5] >> (kb & 31)) & 1u)) continue;   // block-uniform
     __syncthreads();
     if (threadIdx.x < kF32Keys) {
       const int key = key0 + threadIdx.x;
@@ -487,50 +664,54 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32(
   }
 }
 
-template <int D, bool IDX>
+template <int D, bool IDX, bool BS>
 hipError_t run_bf16(const Shape& sh, const void* q, const void* k, const void* v,
-                    const int32_t* budget, const int32_t* idx, int kv_group, void* o,
-                    hipStream_t st) {
+                    const int32_t* budget, const int32_t* idx, const uint32_t* bmask,
+                    int kv_group, void* o, hipStream_t st) {
   const float c = kLog2e / sqrtf(float(D));
   dim3 grid((sh.L + kBM - 1) / kBM, sh.B * sh.Hq);
-  attn_fwd_bf16<D, IDX><<<grid, kThreads, 0, st>>>(
+  attn_fwd_bf16<D, IDX, BS><<<grid, kThreads, 0, st>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), budget, idx, static_cast<uint16_t*>(o), sh.Hq,
+      static_cast<const uint16_t*>(v), budget, idx, bmask, static_cast<uint16_t*>(o), sh.Hq,
       sh.Hq / kv_group, kv_group, sh.L, sh.bud_b(), sh.bud_h(), c);
   return hipGetLastError();
 }
 
-template <int D, bool IDX>
+template <int D, bool IDX, bool BS>
 hipError_t run_f32(const Shape& sh, const void* q, const void* k, const void* v,
-                   const int32_t* budget, const int32_t* idx, int kv_group, void* o,
-                   hipStream_t st) {
+                   const int32_t* budget, const int32_t* idx, const uint32_t* bmask, int kv_group,
+                   void* o, hipStream_t st) {
   const float c = kLog2e / sqrtf(float(D));
   dim3 grid((sh.L + kF32Rows - 1) / kF32Rows, sh.B * sh.Hq);
-  attn_fwd_f32<D, IDX><<<grid, kF32Rows, 0, st>>>(
+  attn_fwd_f32<D, IDX, BS><<<grid, kF32Rows, 0, st>>>(
       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-      budget, idx, static_cast<float*>(o), sh.Hq, sh.Hq / kv_group, kv_group, sh.L, sh.bud_b(),
-      sh.bud_h(), c);
+      budget, idx, bmask, static_cast<float*>(o), sh.Hq, sh.Hq / kv_group, kv_group, sh.L,
+      sh.bud_b(), sh.bud_h(), c);
   return hipGetLastError();
 }
 
-template <bool IDX>
+template <bool IDX, bool BS>
 hipError_t run(const Shape& sh, const void* q, const void* k, const void* v,
-               const int32_t* budget, const int32_t* idx, int kv_group, void* o,
-               hipStream_t st) {
+               const int32_t* budget, const int32_t* idx, const uint32_t* bmask, int kv_group,
+               void* o, hipStream_t st) {
   if (sh.dtype == TSA_BF16)
-    return sh.d == 128 ? run_bf16<128, IDX>(sh, q, k, v, budget, idx, kv_group, o, st)
-                       : run_bf16<64, IDX>(sh, q, k, v, budget, idx, kv_group, o, st);
-  return sh.d == 128 ? run_f32<128, IDX>(sh, q, k, v, budget, idx, kv_group, o, st)
-                     : run_f32<64, IDX>(sh, q, k, v, budget, idx, kv_group, o, st);
+    return sh.d == 128 ? run_bf16<128, IDX, BS>(sh, q, k, v, budget, idx, bmask, kv_group, o, st)
+                       : run_bf16<64, IDX, BS>(sh, q, k, v, budget, idx, bmask, kv_group, o, st);
+  return sh.d == 128 ? run_f32<128, IDX, BS>(sh, q, k, v, budget, idx, bmask, kv_group, o, st)
+                     : run_f32<64, IDX, BS>(sh, q, k, v, budget, idx, bmask, kv_group, o, st);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const void* v,
                             const int32_t* budget, const int32_t* idx, int kv_group, void* o,
-                            hipStream_t st) {
-  return idx ? run<true>(sh, q, k, v, budget, idx, kv_group, o, st)
-             : run<false>(sh, q, k, v, budget, nullptr, kv_group, o, st);
+                            hipStream_t st, const uint32_t* bmask) {
+  if (bmask) {
+    if (idx) return hipErrorInvalidValue;     // block-sparse runs on the compact tensors
+    return run<false, true>(sh, q, k, v, budget, nullptr, bmask, kv_group, o, st);
+  }
+  return idx ? run<true, false>(sh, q, k, v, budget, idx, nullptr, kv_group, o, st)
+             : run<false, false>(sh, q, k, v, budget, nullptr, nullptr, kv_group, o, st);
 }
 
 }  // namespace tsa

@@ -252,6 +252,32 @@ tsa_status tsa_attention(const tsa_problem* prob, const void* q, const void* k, 
       "tsa_attention");
 }
 
+size_t tsa_block_mask_words(const tsa_problem* prob) {
+  tsa::Shape s;
+  if (check_problem(prob, &s) != TSA_OK) return 0;
+  const size_t nb = (size_t(s.L) + 63) / 64, nw = (nb + 31) / 32;
+  return size_t(s.B) * s.Hq * nb * nw;
+}
+
+tsa_status tsa_attention_block_sparse(const tsa_problem* prob, const void* q, const void* k,
+                                      const void* v, const int32_t* budget, int32_t kv_group,
+                                      const uint32_t* block_mask, void* o, void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_problem(prob, &sh));
+  TSA_TRY(check_ptr(q, "q"));
+  TSA_TRY(check_ptr(k, "k"));
+  TSA_TRY(check_ptr(v, "v"));
+  TSA_TRY(check_ptr(o, "o"));
+  TSA_TRY(check_ptr(block_mask, "block_mask"));
+  if (budget && !aligned16(budget)) return fail(TSA_ERR_INVALID_ARG, "budget is not 16-byte aligned");
+  if (kv_group < 1 || sh.Hq % kv_group != 0)
+    return fail(TSA_ERR_INVALID_ARG, "kv_group=%d must be >= 1 and divide Hq=%d", kv_group, sh.Hq);
+  if (fault_injected()) return injected("tsa_attention_block_sparse");
+  return launched(tsa::launch_attention(sh, q, k, v, budget, nullptr, kv_group, o,
+                                        hipStream_t(stream), block_mask),
+                  "tsa_attention_block_sparse");
+}
+
 tsa_status tsa_scatter(const tsa_problem* prob, const void* oc, const int32_t* rank, void* o,
                        void* stream) {
   tsa::Shape sh;

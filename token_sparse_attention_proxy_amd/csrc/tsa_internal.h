@@ -72,9 +72,11 @@ hipError_t launch_gather(const Shape& s, const void* q, const void* k, const voi
 // compact).  Otherwise they are full-length sequence tensors and compact
 // row i of head (b,h) is sequence row idx[b,h,i]; only those rows of o are
 // written.
+// bmask != nullptr: block-sparse attention on compact tensors (idx must be
+// nullptr); see attn_fwd_bf16 for the mask layout.
 hipError_t launch_attention(const Shape& s, const void* q, const void* k, const void* v,
                             const int32_t* budget, const int32_t* idx, int kv_group, void* o,
-                            hipStream_t st);
+                            hipStream_t st, const uint32_t* bmask = nullptr);
 hipError_t launch_zero_unselected(const Shape& s, const int32_t* rank, void* o, hipStream_t st);
 hipError_t launch_scatter(const Shape& s, const void* oc, const int32_t* rank, void* o,
                           hipStream_t st);

@@ -185,3 +185,45 @@ def make_dense(shape, seed: int, dtype: str = "bf16", scale: float = 1.0) -> np.
     rng = np.random.default_rng(seed)
     x = (rng.standard_normal(shape, dtype=np.float32) * np.float32(scale))
     return _to_storage(x, dtype)
+
+
+def make_block_mask(B: int, H: int, L: int, seed: int, pattern: str = "random",
+                    density: float = 0.5, band: int = 4, columns: int = 8) -> np.ndarray:
+    """A seeded block mask for the block-sparse composition, packed as the library
+    takes it: uint32 [B,H,NB,NW] with NB = ceil(L/64), NW = ceil(NB/32); bit
+    kb % 32 of word [b,h,qb,kb // 32] marks key block kb visible to query block qb.
+
+    Patterns (only blocks below the diagonal are drawn; the rest is left 0):
+      "random":         each block visible with probability ``density``;
+      "vertical_slash": the ``band`` blocks just below the diagonal plus
+                        ``columns`` key-block columns drawn per (b, h), the
+                        shape of the sparse prefill patterns the compressed
+                        tensors are combined with;
+      "none" / "all":   no block / every block.
+    """
+    rng = np.random.default_rng(seed)
+    nb = (L + 63) // 64
+    nw = (nb + 31) // 32
+    vis = np.zeros((B, H, nb, nb), dtype=bool)
+    below = np.tril(np.ones((nb, nb), dtype=bool), k=-1)
+    for b in range(B):
+        for h in range(H):
+            if pattern == "random":
+                m = rng.random((nb, nb)) < density
+            elif pattern == "vertical_slash":
+                m = np.zeros((nb, nb), dtype=bool)
+                for off in range(1, band + 1):
+                    m |= np.eye(nb, k=-off, dtype=bool)
+                cols = rng.choice(nb, size=min(columns, nb), replace=False)
+                m[:, cols] = True
+            elif pattern == "all":
+                m = np.ones((nb, nb), dtype=bool)
+            elif pattern == "none":
+                m = np.zeros((nb, nb), dtype=bool)
+            else:
+                raise ValueError(pattern)
+            vis[b, h] = m & below
+    words = np.zeros((B, H, nb, nw), dtype=np.uint64)
+    for kb in range(nb):
+        words[..., kb // 32] |= vis[..., kb].astype(np.uint64) << np.uint64(kb % 32)
+    return words.astype(np.uint32)

@@ -145,6 +145,25 @@ def tsa_attention(prob: Problem, q, k, v, budget=None, kv_group: int = 1, o=None
     return o
 
 
+def block_mask_words(prob: Problem) -> int:
+    return int(_lib.load().tsa_block_mask_words(ctypes.byref(prob.c())))
+
+
+def tsa_attention_block_sparse(prob: Problem, q, k, v, block_mask, budget=None, kv_group: int = 1,
+                               o=None):
+    """block_mask: int32/uint32-valued tensor of block_mask_words(prob) words
+    ([B,Hq,NB,NW]), bit kb % 32 of word [b,h,qb,kb // 32]."""
+    lib = _lib.load()
+    p = prob.c()
+    if block_mask.numel() != block_mask_words(prob) or block_mask.element_size() != 4:
+        raise ValueError("block_mask must hold block_mask_words(prob) 32-bit words")
+    o = _empty(q.shape, q.dtype, q) if o is None else o
+    check(lib.tsa_attention_block_sparse(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(budget),
+                                         kv_group, _ptr(block_mask), _ptr(o), _stream(q.device)),
+          "tsa_attention_block_sparse")
+    return o
+
+
 def tsa_scatter(prob: Problem, oc, rank, o=None):
     lib = _lib.load()
     p = prob.c()
@@ -207,5 +226,6 @@ def forward(q, k, v, w: int, tau: float, fused: bool = False, flags: int = 0):
 __all__ = ["Problem", "TsaError", "workspace_bytes", "forward_workspace_bytes",
            "fused_workspace_bytes", "tsa_score", "tsa_budget", "tsa_select", "tsa_gather",
            "tsa_attention", "tsa_scatter", "tsa_forward", "tsa_attention_indexed",
-           "tsa_forward_fused", "tsa_zero_unselected", "forward", "TSA_FLAG_NONCAUSAL_PROXY",
+           "tsa_forward_fused", "tsa_zero_unselected", "block_mask_words",
+           "tsa_attention_block_sparse", "forward", "TSA_FLAG_NONCAUSAL_PROXY",
            "TSA_FLAG_PER_HEAD_BUDGET", "TSA_FLAG_KEEP_WINDOW"]
