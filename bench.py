@@ -333,7 +333,7 @@ def main():
     flops = attention_flops(bud, wl.Hq, wl.d)
     attn_step = "attention_indexed" if args.path == "fused" else "attention"
     kname = ("attn_fwd_bf16" if bf16 else "attn_fwd_f32") + \
-        (f"<{wl.d}, true>" if args.path == "fused" else f"<{wl.d}, false>")
+        (f"<{wl.d}, true, false>" if args.path == "fused" else f"<{wl.d}, false, false>")
     achieved = flops / (steps_ms[attn_step] * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     traffic = measured_traffic(kname, wl.name) if bf16 else None

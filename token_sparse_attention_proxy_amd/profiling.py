@@ -15,7 +15,8 @@ Two sub-commands, meant to run under rocprofv3 and after it:
   python -m token_sparse_attention_proxy_amd.profiling summarize \\
         --fetch DIR --write DIR --workload NAME --budget K --path P [--out profiles/traffic.json]
       Reads the two counter CSVs, scales each counter by what it reads for
-      the copy (bytes moved / counter bytes), and records the attention
+      the copy (bytes moved / counter bytes; the copy is the runtime's
+      device-to-device blit kernel), and records the attention
       kernel's HBM bytes per launch, keyed by the kernel source hash, so that
       bench.py reports them only while the kernel is unchanged.
 """
@@ -95,12 +96,12 @@ def _pick(rows, needle):
 def cmd_summarize(args):
     fetch = _read(args.fetch, "FETCH_SIZE")
     write = _read(args.write, "WRITE_SIZE")
-    # the copy is the largest-FETCH non-attention kernel
-    copy_f = max(v for n, v in fetch if "attn_fwd" not in n) * 1024.0
-    copy_w = max(v for n, v in write if "attn_fwd" not in n) * 1024.0
+    # the calibration copy is the runtime's device-to-device blit of COPY_BYTES
+    copy_f = max(_pick(fetch, "copyBuffer")) * 1024.0
+    copy_w = max(_pick(write, "copyBuffer")) * 1024.0
     f_scale = COPY_BYTES / copy_f
     w_scale = COPY_BYTES / copy_w
-    kname = f"attn_fwd_bf16<{args.d}, {'true' if args.path == 'fused' else 'false'}>"
+    kname = f"attn_fwd_bf16<{args.d}, {'true' if args.path == 'fused' else 'false'}, false>"
     af = _pick(fetch, kname)
     aw = _pick(write, kname)
     fetch_b = sum(af) / len(af) * 1024.0 * f_scale
