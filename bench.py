@@ -20,7 +20,11 @@ Printed as one JSON line, with:
     timed path under each, against the same dense baseline;
   * the block-sparse composition: the attention on the compressed tensors
     under seeded block masks of several densities (ms, visible fraction,
-    TFLOP/s on the visible block pairs).
+    TFLOP/s on the visible block pairs);
+  * a synthetic 4-layer stack with random weights at the 32K shape (Hq=32,
+    Hkv=8, d=128): every layer re-selects; per-layer K/L, overlap of the
+    index sets of consecutive layers, and the stack's time against the same
+    stack with dense attention.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--path fused|steps]
@@ -153,6 +157,7 @@ def main():
     ap.add_argument("--path", choices=["fused", "steps"], default="steps")
     ap.add_argument("--no-readings", action="store_true")
     ap.add_argument("--no-block-sparse", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -328,6 +333,39 @@ def main():
                 f"{block_sparse[name]['TFLOP_s']} TFLOP/s")
             del md
 
+    # ---- synthetic multi-layer stack: re-selection in every layer
+    stack_rep = None
+    if not args.no_stack:
+        from token_sparse_attention_proxy_amd import stack as S
+        scfg = S.StackConfig(B=1, L=32768, Hq=32, Hkv=8, d=128, layers=4, w=64, tau=0.05,
+                             fused=args.path == "fused")
+        sg = torch.Generator(device=dev).manual_seed(4321)
+        sx = torch.randn((scfg.B, scfg.L, scfg.model_dim), generator=sg, device=dev).to(torch.bfloat16)
+        sw = S.make_weights(scfg, seed=4322, device=dev)
+
+        def stack_ms(dense):
+            S.run_stack(scfg, sx, sw, dense=dense)
+            torch.cuda.synchronize()
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(st)
+            for _ in range(2):
+                out = S.run_stack(scfg, sx, sw, dense=dense)
+            s1.record(st)
+            torch.cuda.synchronize()
+            return s0.elapsed_time(s1) / 2, out[1]
+        tsa_ms, recs = stack_ms(False)
+        dense_stack_ms, _ = stack_ms(True)
+        kl = [round(float(r["budget"].float().mean()) / scfg.L, 4) for r in recs]
+        stack_rep = {"config": dataclasses.asdict(scfg), "ms_tsa": round(tsa_ms, 3),
+                     "ms_dense": round(dense_stack_ms, 3),
+                     "speedup": round(dense_stack_ms / tsa_ms, 4), "keep_frac_per_layer": kl,
+                     "reselection": [{k2: (round(v2, 4) if v2 is not None else None) for k2, v2 in r.items()}
+                                     for r in S.reselection(scfg, recs)],
+                     "note": "random weights, projections by torch.matmul; no accuracy claim"}
+        log(f"[bench] stack: {tsa_ms:.2f} ms vs dense {dense_stack_ms:.2f} ms, K/L {kl}, "
+            f"reselection {stack_rep['reselection']}")
+        del sx, sw, recs
+
     # ---- roofline of the dominant kernel (the timed path's attention), algorithmic FLOPs
     bf16 = wl.dtype == "bf16"
     flops = attention_flops(bud, wl.Hq, wl.d)
@@ -401,6 +439,7 @@ def main():
         "roofline": roofline,
         "readings": readings,
         "block_sparse": block_sparse,
+        "stack": stack_rep,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
