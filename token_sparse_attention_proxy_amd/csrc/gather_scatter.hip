@@ -5,7 +5,8 @@
 // scatter: for every j < L, o[b,h,j] = rank_j >= 0 ? oc[b,h,rank_j] : 0
 //
 // Both are pure byte movement: rows are copied as 16-byte vectors, one row
-// per group of lanes.  The scatter is destination-driven, so each output
+// per group of lanes, with streaming (non-temporal) stores: the outputs are
+// not read again by these kernels.  The scatter is destination-driven, so each output
 // row is written exactly once (copied or zero-filled) and coalesced.
 //
 // zero_unselected: o[b,h,j] = 0 for every j with rank_j < 0.  It is the part
@@ -43,18 +44,30 @@ __global__ __launch_bounds__(kThreads) void gather_rows(
     if (i0 >= n) continue;
     const int i1 = min(i0 + kRowsPerBlock, n);
     const int64_t hrow = (int64_t(b) * Hq + h) * L;   // first row of (b,h)
-    for (int i = i0 + sub; i < i1; i += kRowsPerPass) {
-      const int src = idx[hrow + i];
-      const int64_t dst = (hrow + i) * VPR + vec;
-      if (src >= 0 && src < L) {
-        qc[dst] = q[(hrow + src) * VPR + vec];
-        kc[dst] = k[(grow + src) * VPR + vec];
-        vc[dst] = v[(grow + src) * VPR + vec];
-      } else {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        qc[dst] = z;
-        kc[dst] = z;
-        vc[dst] = z;
+    constexpr int R = kRowsPerBlock / kRowsPerPass;   // rows per thread, all loads first
+    int src[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = i0 + sub + r * kRowsPerPass;
+      src[r] = i < i1 ? idx[hrow + i] : -1;
+    }
+    u32x4 aq[R], ak[R], av[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const bool ok = src[r] >= 0 && src[r] < L;
+      aq[r] = ok ? q[(hrow + src[r]) * VPR + vec] : z;
+      ak[r] = ok ? k[(grow + src[r]) * VPR + vec] : z;
+      av[r] = ok ? v[(grow + src[r]) * VPR + vec] : z;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = i0 + sub + r * kRowsPerPass;
+      if (i < i1) {
+        const int64_t dst = (hrow + i) * VPR + vec;
+        __builtin_nontemporal_store(aq[r], qc + dst);
+        __builtin_nontemporal_store(ak[r], kc + dst);
+        __builtin_nontemporal_store(av[r], vc + dst);
       }
     }
   }
@@ -73,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void scatter_rows(const u32x4* __restrict
     const int r = rank[hrow + j];
     u32x4 val = {0u, 0u, 0u, 0u};
     if (r >= 0 && r < L) val = oc[(hrow + r) * VPR + vec];
-    o[(hrow + j) * VPR + vec] = val;
+    __builtin_nontemporal_store(val, o + (hrow + j) * VPR + vec);
   }
 }
 
@@ -86,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void zero_rows(const int32_t* __restrict_
   const int sub = threadIdx.x / VPR, vec = threadIdx.x % VPR;
   const int64_t hrow = int64_t(bh) * L;
   for (int j = j0 + sub; j < min(j0 + kRowsPerBlock, L); j += kRowsPerPass) {
-    if (rank[hrow + j] < 0) o[(hrow + j) * VPR + vec] = u32x4{0u, 0u, 0u, 0u};
+    if (rank[hrow + j] < 0) __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, o + (hrow + j) * VPR + vec);
   }
 }
 
