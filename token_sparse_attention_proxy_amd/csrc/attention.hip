@@ -18,10 +18,13 @@
 //     bf16, is directly the B operand of O^T = V^T P^T;
 //   * V is transposed in registers while staged, so LDS holds V^T and the
 //     A operand of the PV product is one 16-byte LDS read per lane;
-//   * softmax with a fixed per-row reference: p = exp2(S log2(e)/sqrt(d) - m)
-//     where m is the row max over the first key tile.  The loop then needs
-//     no running max, no cross-lane reduction and no rescaling of O, which
-//     stays in accumulator registers touched only by MFMA: one FMA, one
+//   * Q is scaled by c = log2(e)/sqrt(d) once, when the wave loads it, and
+//     rounded to bf16, so S^T comes out of the MFMA in log2 units;
+//   * softmax with a fixed per-row reference: p = exp2(S - m) where m is the
+//     row max over the first key tile.  Every later S^T chain starts from
+//     an accumulator holding -m, so the subtraction costs nothing, and the
+//     loop needs no running max, no cross-lane reduction and no rescaling
+//     of O, which stays in accumulator registers touched only by MFMA: one
 //     exp2, one add and half a bf16 pack per score.  Softmax is invariant
 //     to the reference, so the result equals the usual one up to rounding.
 //     A row sum above 2^64 (a later logit far above the first tile's max)
@@ -146,6 +149,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     qf[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                            rq, (qsrc * D + 16 * t + 8 * half) * 2, 0, 0));
 
+  // Q^T pre-scaled by c = log2(e)/sqrt(d) and rounded to bf16, so the S^T
+  // accumulators are logits in log2 units.
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    u32x4 w = __builtin_bit_cast(u32x4, qf[t]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = pack_bf16x2(__uint_as_float(w[e] << 16) * c, __uint_as_float(w[e] & 0xffff0000u) * c);
+    qf[t] = __builtin_bit_cast(bf16x8, w);
+  }
   const int kv_end = min(q0 + kBM, n);
   const int ntiles = (kv_end + kBN - 1) / kBN;
 
@@ -236,13 +249,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   const f32x16 zero = {};
 
   // S^T = K Q^T for the tile in `buf`: two independent accumulator chains.
-  auto qk = [&](int buf, f32x16 (&sacc)[NSUB]) {
+  auto qk = [&](int buf, f32x16 (&sacc)[NSUB], const f32x16& init) {
 #pragma unroll
     for (int t = 0; t < KS; ++t)
 #pragma unroll
       for (int sb = 0; sb < NSUB; ++sb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * sb + krow][16 * t + 8 * half]);
-        sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? zero : sacc[sb], 0, 0, 0);
+        sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? init : sacc[sb], 0, 0, 0);
       }
   };
   auto mask = [&](int key0, f32x16 (&sacc)[NSUB]) {
@@ -263,11 +276,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
 
   f32x16 oacc[DT];
   float m_ref = 0.f;      // exp2 reference of this lane's row
+  f32x16 bias = zero;     // -m_ref in every element: the S^T chains start from it
+  auto set_ref = [&](float m) {
+    m_ref = m;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) bias[e] = -m;
+  };
   float l_run = 0.f;      // this lane's share of the row sum
 
-  // P = exp2(S c - m_ref), row sums, then O^T += V^T P^T.
-  auto pv = [&](int buf, const f32x16 (&sacc)[NSUB]) {
-    const float mneg = -m_ref;
+  // P = exp2(S - m_ref) (biased: S^T already holds -m_ref from its chain start),
+  // row sums, then O^T += V^T P^T.
+  auto pv = [&](int buf, const f32x16 (&sacc)[NSUB], bool biased) {
+    const float mneg = biased ? 0.f : -m_ref;
     bf16x8 pb[NSUB * 2];
     float ls[4] = {0.f, 0.f, 0.f, 0.f};      // independent partial sums
 #pragma unroll
@@ -277,8 +297,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
         u32x4 pk;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[sb][8 * tt + 2 * e2], c, mneg));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[sb][8 * tt + 2 * e2 + 1], c, mneg));
+          const float p0 = __builtin_amdgcn_exp2f(sacc[sb][8 * tt + 2 * e2] + mneg);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[sb][8 * tt + 2 * e2 + 1] + mneg);
           ls[(2 * e2) & 3] += p0;
           ls[(2 * e2 + 1) & 3] += p1;
           pk[e2] = pack_bf16x2(p0, p1);
@@ -309,7 +329,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     constexpr int LAST_SLOT = 2 * LAST * DT;  // PV MFMAs that can carry the last subtile's softmax
     constexpr int LPP = (8 + LAST_SLOT - 1) / LAST_SLOT;   // its pairs per carrying MFMA
     static_assert(LAST >= 1 && 8 % KS == 0, "pipeline shape");
-    const float mneg = -m_ref;
     const uint16_t* kbase = &sm.k[buf][krow][8 * half];
     const uint16_t* vbase = &sm.vt[buf][l32][8 * half];
     auto rd = [&](int r) {
@@ -322,8 +341,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     u32x4 pk[2 * NSUB];
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
     auto softmax_pair = [&](int sb, int p) {  // elements 2p, 2p+1 of subtile sb
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[sb][2 * p], c, mneg));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[sb][2 * p + 1], c, mneg));
+      const float p0 = __builtin_amdgcn_exp2f(sacc[sb][2 * p]);
+      const float p1 = __builtin_amdgcn_exp2f(sacc[sb][2 * p + 1]);
       ls[(2 * p) & 3] += p0;
       ls[(2 * p + 1) & 3] += p1;
       pk[2 * sb + p / 4][p % 4] = pack_bf16x2(p0, p1);
@@ -337,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
       const bf16x8 a = ring[m % (PF + 1)];
       if (m < NQK) {
         const int sb = m / KS, t = m % KS;
-        sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? zero : sacc[sb], 0, 0, 0);
+        sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? bias : sacc[sb], 0, 0, 0);
         if (sb >= 1) {                        // softmax of subtile sb-1, 8/KS pairs per MFMA
 #pragma unroll
           for (int p = t * (8 / KS); p < (t + 1) * (8 / KS); ++p) softmax_pair(sb - 1, p);
@@ -464,7 +483,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
           if (nxt < ntiles) load_tile(nxt);
           if (use_cur) {
             f32x16 sacc[NSUB];
-            qk(buf, sacc);
+            qk(buf, sacc, zero);
             if (cur == wdiag) mask(cur * kBN, sacc);
             m = fmaxf(m, tile_max(sacc));
           }
@@ -477,7 +496,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
           use_nxt = use_nxt2;
           buf ^= 1;
         }
-        m_ref = m * c;
+        set_ref(m);
       }
 #pragma unroll
       for (int i = 0; i < DT; ++i) oacc[i] = zero;
@@ -499,10 +518,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
             hot(buf);
           } else {
             f32x16 sacc[NSUB];
-            qk(buf, sacc);
+            qk(buf, sacc, have_ref ? bias : zero);
             if (cur == wdiag) mask(cur * kBN, sacc);
-            if (!have_ref) m_ref = tile_max(sacc) * c;
-            pv(buf, sacc);
+            if (!have_ref) set_ref(tile_max(sacc));
+            pv(buf, sacc, have_ref);
           }
           have_ref = true;
         }
@@ -530,14 +549,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
         if (IDX) read_rows(tile + 2);
         if (tile <= wdiag) {
           f32x16 sacc[NSUB];
-          qk(buf, sacc);
+          qk(buf, sacc, zero);
           if (tile == wdiag) mask(tile * kBN, sacc);
           m = fmaxf(m, tile_max(sacc));
         }
         if (tile + 1 < ntiles) store_tile(buf ^ 1);
         __syncthreads();
       }
-      m_ref = m * c;
+      set_ref(m);
     }
 #pragma unroll
     for (int i = 0; i < DT; ++i) oacc[i] = zero;
@@ -552,11 +571,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
       if (tile < wdiag && tile > 0) {
         hot(buf);                       // no mask, no reductions
       } else if (tile <= wdiag) {
+        const bool ref_tile = tile == 0 && attempt == 0;
         f32x16 sacc[NSUB];
-        qk(buf, sacc);
+        qk(buf, sacc, ref_tile ? zero : bias);
         if (tile == wdiag) mask(tile * kBN, sacc);
-        if (tile == 0 && attempt == 0) m_ref = tile_max(sacc) * c;
-        pv(buf, sacc);
+        if (ref_tile) set_ref(tile_max(sacc));
+        pv(buf, sacc, !ref_tile);
       }
       if (tile + 1 < ntiles) store_tile(buf ^ 1);
       __syncthreads();
