@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     constexpr int NQK = NSUB * KS;            // S^T MFMAs, chain after chain
     constexpr int NPV = 2 * NSUB * DT;        // O^T MFMAs, kk-major
     constexpr int NR = NQK + NPV;             // operand reads, in MFMA order
-    constexpr int PF = 2;
+    constexpr int PF = 3;
     constexpr int LAST = NSUB - 1;
     constexpr int LAST_SLOT = 2 * LAST * DT;  // PV MFMAs that can carry the last subtile's softmax
     constexpr int LPP = (8 + LAST_SLOT - 1) / LAST_SLOT;   // its pairs per carrying MFMA
