@@ -510,8 +510,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
       store_tile(0);
       __syncthreads();
       while (true) {
-        const int nxt2 = nxt < ntiles ? next_from(nxt + 1) : ntiles;     // before the K/V loads
-        const bool use_nxt2 = nxt2 < ntiles && wave_uses(nxt2);
         if (nxt < ntiles) load_tile(nxt);
         if (use_cur) {
           if (cur < wdiag && have_ref) {
@@ -525,6 +523,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
           }
           have_ref = true;
         }
+        // The walk's bookkeeping for the iteration after next runs while this
+        // tile's last MFMAs drain, not in front of the next tile's work.
+        const int nxt2 = nxt < ntiles ? next_from(nxt + 1) : ntiles;
+        const bool use_nxt2 = nxt2 < ntiles && wave_uses(nxt2);
         if (nxt < ntiles) store_tile(buf ^ 1);
         __syncthreads();
         if (nxt >= ntiles) break;
