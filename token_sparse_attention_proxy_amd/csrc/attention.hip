@@ -386,8 +386,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   // qb0 .. qb0 + QB - 1; each wave's query block is its diagonal tile.  The
   // walk keeps a cursor on one 32-tile word of the mask: the four rows' words
   // of the current word are in registers and those of the next word are
-  // prefetched, so finding the next tile and whether a wave uses it is
-  // register arithmetic; only a run of empty words costs a wait.  Mask words
+  // prefetched.  When the cursor steps onto a word, the tiles of that word
+  // the workgroup needs and those this wave uses are folded into two
+  // wave-uniform bit sets, so finding the next tile and whether a wave uses
+  // it is a few scalar operations; only a run of empty words costs a wait.  Mask words
   // are read with buffer (vector-memory) loads, which never share a wait
   // counter with the LDS operand reads of the MFMA loop.
   constexpr int QB = kBM / kBN;
@@ -398,6 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   const int wsel = wdiag - qb0;          // this wave's row among the QB (0 .. QB-1)
   int wd_cur = 0;                        // word under the cursor
   uint32_t rw_cur[QB], rw_nxt[QB];       // row words of word wd_cur and wd_cur + 1
+  uint32_t u_cur = 0, w_cur = 0;         // of word wd_cur: tiles needed, tiles this wave's row sees
   auto load_word = [&](int wd, uint32_t (&rw)[QB]) {   // rows past NB read as 0 (outside the buffer)
     const bool in = wd < NW;
 #pragma unroll
@@ -421,9 +424,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     u = (u & ~from_a) | from_a;          // tiles >= qb0 are always needed
     return __builtin_amdgcn_readfirstlane(u & below_e);
   };
+  auto set_word = [&]() {                // fold the cursor's row words into u_cur, w_cur
+    u_cur = needed_bits(wd_cur, rw_cur);
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < QB; ++i) w = (i == wsel) ? rw_cur[i] : w;
+    w_cur = __builtin_amdgcn_readfirstlane(w);
+  };
   auto next_from = [&](int p) {          // first needed tile >= p; moves the cursor to it
     if ((p >> 5) == wd_cur) {
-      const uint32_t u = needed_bits(wd_cur, rw_cur) & (~0u << (p & 31));
+      const uint32_t u = u_cur & (~0u << (p & 31));
       if (u) return (wd_cur << 5) + __builtin_ctz(u);
       p = (wd_cur + 1) << 5;
     }
@@ -432,7 +442,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
 #pragma unroll
       for (int i = 0; i < QB; ++i) rw_cur[i] = rw_nxt[i];
       load_word(wd_cur + 1, rw_nxt);
-      const uint32_t u = needed_bits(wd_cur, rw_cur) & (~0u << (p & 31));
+      set_word();
+      const uint32_t u = u_cur & (~0u << (p & 31));
       if (u) return (wd_cur << 5) + __builtin_ctz(u);
       p = (wd_cur + 1) << 5;
     }
@@ -440,7 +451,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
       wd_cur = p >> 5;
       load_word(wd_cur, rw_cur);
       load_word(wd_cur + 1, rw_nxt);
-      const uint32_t u = needed_bits(wd_cur, rw_cur) & (~0u << (p & 31));
+      set_word();
+      const uint32_t u = u_cur & (~0u << (p & 31));
       if (u) return (wd_cur << 5) + __builtin_ctz(u);
       p = (wd_cur + 1) << 5;
     }
@@ -450,15 +462,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     if (t > wdiag) return false;
     if (t == wdiag || !BS) return true;
     if (wdiag >= NB) return false;       // a wave past the last row
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < QB; ++i) w = (i == wsel) ? rw_cur[i] : w;
-    return ((__builtin_amdgcn_readfirstlane(w) >> (t & 31)) & 1u) != 0;
+    return ((w_cur >> (t & 31)) & 1u) != 0;
   };
   auto begin_bs = [&]() {                // cursor on word 0; returns the first tile
     wd_cur = 0;
     load_word(0, rw_cur);
     load_word(1, rw_nxt);
+    set_word();
     return next_from(0);
   };
 
