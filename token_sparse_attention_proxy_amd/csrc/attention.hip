@@ -37,7 +37,7 @@
 //     branches;
 //   * only each wave's diagonal tile is masked; tiles above it are skipped;
 //   * query blocks are issued heaviest first (the causal triangle), across
-//     groups of 8 heads;
+//     groups of 8 KV heads, each KV head's query heads on one XCD;
 //   * block-sparse composition (BS): a caller's bit mask over (64-row query
 //     block, 64-key block) pairs of the compressed sequence says which key
 //     tiles each query block sees (its diagonal block always).  A workgroup
@@ -57,7 +57,7 @@ constexpr int kBM = 32 * kWaves;  // query rows per workgroup: 32 per wave
 constexpr int kBN = 64;           // keys per tile
 constexpr int kKPad = 8;          // bf16 elements of padding per K row in LDS
 constexpr int kVPad = 8;          // bf16 elements of padding per V^T row in LDS
-constexpr int kHeadGroup = 8;     // heads whose query blocks are interleaved in dispatch order
+constexpr int kXcds = 8;          // workgroups go round-robin to the 8 XCDs in dispatch order
 // A row sum above 2^64 means some exponent relative to the reference max
 // may have overflowed or lost range: the workgroup then recomputes with the
 // exact row max as reference.
@@ -122,16 +122,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, half = lane >> 5;
-  // Dispatch order: heads in groups of kHeadGroup; within a group, the
-  // heaviest query blocks of all its heads first.  Each group then ends on
-  // light blocks (no long block starts near the end), while the workgroups
-  // in flight share the K/V of only a few heads in L2.
+  // Dispatch order: heads in groups of 8 KV heads (8 * kv_group query
+  // heads); within a group, the heaviest query blocks of all its heads
+  // first, so each group ends on light blocks and no long block starts near
+  // the end.  Workgroups go to the XCDs round-robin, so linear position
+  // mod 8 picks the XCD: every query head of one KV head lands on the same
+  // XCD and its L2 serves that head's K and V alone.
   const int nqb = (L + kBM - 1) / kBM;
   const int lin = int(blockIdx.x) + int(blockIdx.y) * nqb;
-  const int grp = lin / (kHeadGroup * nqb);
-  const int hg = min(kHeadGroup, int(gridDim.y) - grp * kHeadGroup);
-  const int rem = lin - grp * kHeadGroup * nqb;
-  const int bh = grp * kHeadGroup + rem % hg;
+  const int G8 = kXcds * kv_group;
+  const int grp = lin / (G8 * nqb);
+  const int hg = min(G8, int(gridDim.y) - grp * G8);
+  const int rem = lin - grp * G8 * nqb;
+  const int bh = grp * G8 + (hg == G8 ? (rem % kXcds) * kv_group + (rem / kXcds) % kv_group : rem % hg);
   const int b = bh / Hq, h = bh % Hq;
   const int hk = h / kv_group;
   const int n = budget ? min(max(budget[b * bud_b + h * bud_h], 0), L) : L;
