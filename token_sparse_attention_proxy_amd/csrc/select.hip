@@ -10,8 +10,11 @@
 //   1. radix descent (11/11/10-bit digits) finds T, the K-th largest key;
 //   2. with c_gt = #{key > T} and need = K - c_gt, token j is kept when
 //      key_j > T, or key_j == T and fewer than `need` T-valued tokens
-//      precede it; one block scan per 1024 tokens of the packed
-//      (greater, equal) counts gives every kept token its output slot.
+//      precede it; one block scan per 4096 tokens (four contiguous tokens
+//      per thread) of the packed (greater, equal) counts gives every kept
+//      token its output slot.
+// Both phases walk the scores four contiguous tokens per thread per step,
+// with the next step's loads issued before the current step's work.
 // Only integer operations are involved: results are bit-exact and
 // deterministic.
 //
@@ -26,9 +29,27 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kBuckets = 2048;
+constexpr int kPer = 4;                 // contiguous tokens per thread per step (a multiple of 4)
+constexpr int kStep = kThreads * kPer;
 
 __device__ __forceinline__ uint32_t score_key(float x) {
   return (x > 0.0f) ? __float_as_uint(x) : 0u;   // NaN, -0, negatives -> 0
+}
+
+// Keys of tokens j0 .. j0 + kPer - 1 (0 past nc); one 16-byte load when aligned.
+__device__ __forceinline__ void load_keys(const float* __restrict__ sh, int j0, int nc, bool vec,
+                                          uint32_t (&u)[kPer]) {
+  if (vec && j0 + kPer <= nc) {
+#pragma unroll
+    for (int v = 0; v < kPer / 4; ++v) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(sh + j0 + 4 * v);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) u[4 * v + q] = score_key(x[q]);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) u[q] = j0 + q < nc ? score_key(sh[j0 + q]) : 0u;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void select_topk(const float* __restrict__ s,
@@ -49,6 +70,8 @@ __global__ __launch_bounds__(kThreads) void select_topk(const float* __restrict_
   const float* sh = s + int64_t(bh) * L;
   int32_t* ih = idx + int64_t(bh) * L;
   int32_t* rh = rank + int64_t(bh) * L;
+  const bool vec = (L % kPer) == 0 && (reinterpret_cast<uintptr_t>(s) % 16) == 0 &&
+                   (reinterpret_cast<uintptr_t>(rank) % 16) == 0;   // rows start 16-byte aligned
 
   // ---- 1. the K-th largest key T
   uint32_t prefix = 0, above = 0;
@@ -61,10 +84,18 @@ __global__ __launch_bounds__(kThreads) void select_topk(const float* __restrict_
     for (int i = t; i < kBuckets; i += kThreads) hist[i] = 0;
     if (t == 0) dsel = -1;
     __syncthreads();
-    for (int j = t; j < nc; j += kThreads) {
-      const uint32_t u = score_key(sh[j]);
-      const uint32_t top = hi >= 32 ? 0u : (u >> hi);
-      if (top == prefix) atomicAdd(&hist[(u >> lo) & ((1u << width) - 1u)], 1u);
+    uint32_t u[kPer], un[kPer];
+    load_keys(sh, kPer * t, nc, vec, u);
+    for (int base = 0; base < nc; base += kStep) {
+      load_keys(sh, base + kStep + kPer * t, nc, vec, un);
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const uint32_t top = hi >= 32 ? 0u : (u[q] >> hi);
+        if (base + kPer * t + q < nc && top == prefix)
+          atomicAdd(&hist[(u[q] >> lo) & ((1u << width) - 1u)], 1u);
+      }
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) u[q] = un[q];
     }
     __syncthreads();
     // Thread t owns digits dA = 2047-2t and dB = dA-1 (descending order).
@@ -88,28 +119,45 @@ __global__ __launch_bounds__(kThreads) void select_topk(const float* __restrict_
 
   // ---- 2. ascending compaction
   uint32_t carry_gt = 0, carry_eq = 0;
-  for (int base = 0; base < nc; base += kThreads) {
-    const int j = base + t;
-    uint32_t gt = 0, eq = 0;
-    if (j < nc) {
-      const uint32_t u = score_key(sh[j]);
-      gt = u > T;
-      eq = u == T;
+  uint32_t u[kPer], un[kPer];
+  load_keys(sh, kPer * t, nc, vec, u);
+  for (int base = 0; base < nc; base += kStep) {
+    const int j0 = base + kPer * t;
+    load_keys(sh, j0 + kStep, nc, vec, un);
+    uint32_t gt[kPer], eq[kPer], ngt = 0, neq = 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const bool in = j0 + q < nc;
+      gt[q] = in && u[q] > T;
+      eq[q] = in && u[q] == T;
+      ngt += gt[q];
+      neq += eq[q];
     }
     uint64_t tot;
-    const uint64_t ex = block_excl_scan_u64((uint64_t(gt) << 32) | eq, scan_tmp, &tot);
-    const uint32_t gt_before = carry_gt + uint32_t(ex >> 32);
-    const uint32_t eq_before = carry_eq + uint32_t(ex & 0xffffffffu);
-    if (j < nc) {
-      const bool kept = gt || (eq && eq_before < need);
-      if (kept) {
-        const uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
-        ih[pos] = j;
-        rh[j] = int32_t(pos);
-      } else {
-        rh[j] = -1;
-      }
+    const uint64_t ex = block_excl_scan_u64((uint64_t(ngt) << 32) | neq, scan_tmp, &tot);
+    uint32_t gt_before = carry_gt + uint32_t(ex >> 32);
+    uint32_t eq_before = carry_eq + uint32_t(ex & 0xffffffffu);
+    int32_t rk[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const bool kept = gt[q] || (eq[q] && eq_before < need);
+      const uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
+      if (kept && j0 + q < nc) ih[pos] = j0 + q;
+      rk[q] = kept ? int32_t(pos) : -1;
+      gt_before += gt[q];
+      eq_before += eq[q];
     }
+    if (vec && j0 + kPer <= nc) {
+#pragma unroll
+      for (int v = 0; v < kPer / 4; ++v)
+        *reinterpret_cast<int4*>(rh + j0 + 4 * v) = make_int4(rk[4 * v], rk[4 * v + 1], rk[4 * v + 2], rk[4 * v + 3]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < kPer; ++q)
+        if (j0 + q < nc) rh[j0 + q] = rk[q];
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) u[q] = un[q];
     carry_gt += uint32_t(tot >> 32);
     carry_eq += uint32_t(tot & 0xffffffffu);
   }
