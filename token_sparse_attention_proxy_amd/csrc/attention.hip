@@ -84,10 +84,10 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-template <int D>
+template <int D, int NBUF>
 struct AttnSmem {
-  uint16_t k[2][kBN][D + kKPad];
-  uint16_t vt[2][D][kBN + kVPad];
+  uint16_t k[NBUF][kBN][D + kKPad];
+  uint16_t vt[NBUF][D][kBN + kVPad];
 };
 
 // Key index held in element e of the S^T accumulator of a 32-key subtile, for a lane in `half`.
@@ -116,7 +116,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   constexpr int KS = D / 16;                           // k-steps of S^T
   constexpr int NSUB = kBN / 32;                       // 32-key subtiles
   static_assert(KCH >= 1 && VPAIRS <= kThreads, "tile shape");
-  __shared__ AttnSmem<D> sm;
+  // Dense walk: four tile buffers, one barrier per two tiles.  Indexed and
+  // block-sparse walks: two buffers, one barrier per tile.
+  constexpr int NBUF = (IDX || BS) ? 2 : 4;
+  __shared__ AttnSmem<D, NBUF> sm;
   __shared__ int idx_s[IDX ? 2 : 1][kBN];     // sequence rows of upcoming key tiles
 
   const int tid = threadIdx.x;
@@ -586,13 +589,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
 #pragma unroll
     for (int i = 0; i < DT; ++i) oacc[i] = zero;
     l_run = 0.f;
-    begin_walk();
-    for (int tile = 0; tile < ntiles; ++tile) {
-      const int buf = tile & 1;
-      put_idx(tile + 3, held);
-      held = fetch_idx(tile + 4);                 // before the K/V loads: never waits on them
-      if (tile + 1 < ntiles) load_tile(tile + 1);
-      if (IDX) read_rows(tile + 2);
+    auto compute = [&](int tile, int buf) {
       if (tile < wdiag && tile > 0) {
         hot(buf);                       // no mask, no reductions
       } else if (tile <= wdiag) {
@@ -603,8 +600,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
         if (ref_tile) set_ref(tile_max(sacc));
         pv(buf, sacc, !ref_tile);
       }
-      if (tile + 1 < ntiles) store_tile(buf ^ 1);
+    };
+    if constexpr (NBUF == 4) {
+      // Tiles t and t+1 sit in buffers t%4 and (t+1)%4; tiles t+2 and t+3
+      // are staged into the other two while they are computed, and one
+      // barrier per pair publishes them and frees t and t+1.
+      load_tile(0);
+      store_tile(0);
+      if (1 < ntiles) {
+        load_tile(1);
+        store_tile(1);
+      }
       __syncthreads();
+      for (int t = 0; t < ntiles; t += 2) {
+        if (t + 2 < ntiles) load_tile(t + 2);
+        compute(t, t & 3);
+        if (t + 2 < ntiles) store_tile((t + 2) & 3);
+        if (t + 1 < ntiles) {
+          if (t + 3 < ntiles) load_tile(t + 3);
+          compute(t + 1, (t + 1) & 3);
+          if (t + 3 < ntiles) store_tile((t + 3) & 3);
+        }
+        __syncthreads();
+      }
+    } else {
+      begin_walk();
+      for (int tile = 0; tile < ntiles; ++tile) {
+        const int buf = tile & 1;
+        put_idx(tile + 3, held);
+        held = fetch_idx(tile + 4);               // before the K/V loads: never waits on them
+        if (tile + 1 < ntiles) load_tile(tile + 1);
+        if (IDX) read_rows(tile + 2);
+        compute(tile, buf);
+        if (tile + 1 < ntiles) store_tile(buf ^ 1);
+        __syncthreads();
+      }
     }
     const bool bad = !(sum_halves(l_run) <= kSumLimit);
     if (!__syncthreads_or(bad)) break;
