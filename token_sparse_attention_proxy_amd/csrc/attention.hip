@@ -116,11 +116,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   constexpr int KS = D / 16;                           // k-steps of S^T
   constexpr int NSUB = kBN / 32;                       // 32-key subtiles
   static_assert(KCH >= 1 && VPAIRS <= kThreads, "tile shape");
-  // Dense walk: four tile buffers, one barrier per two tiles.  Indexed and
-  // block-sparse walks: two buffers, one barrier per tile.
-  constexpr int NBUF = (IDX || BS) ? 2 : 4;
+  // Dense and indexed walks: four tile buffers, one barrier per two tiles.
+  // Block-sparse walk: two buffers, one barrier per tile.
+  constexpr int NBUF = BS ? 2 : 4;
   __shared__ AttnSmem<D, NBUF> sm;
-  __shared__ int idx_s[IDX ? 2 : 1][kBN];     // sequence rows of upcoming key tiles
+  __shared__ int idx_s[IDX ? 4 : 1][kBN];     // sequence rows of upcoming key tiles (slot = tile % 4)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -183,27 +183,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   const int vkg = tid % (kBN / 4), vdc = tid / (kBN / 4);   // (key group, d chunk) of this thread
 
   // Indexed staging.  The sequence rows of key tile t are fetched from HBM
-  // (one per thread of wave 0) at the top of iteration t-4, published to a
-  // two-slot LDS ring at the top of iteration t-3, and read into this
-  // thread's row registers early in iteration t-2, under its MFMA work.  The
-  // K/V loads of tile t, issued at the top of iteration t-1, then wait on
-  // nothing, and no index work sits before a barrier.
+  // (one per thread of wave 0) well before they are needed, published to
+  // LDS slot t % 4 before a barrier, and read into this thread's row
+  // registers before the K/V loads of tile t are issued (per-tile walk:
+  // fetched at the top of iteration t-4, published at t-3, read in t-2,
+  // loaded at the top of t-1; paired walk: see there).  The K/V loads then
+  // wait on nothing, and no index work sits before a barrier.
   int krs[KCH], vrs[4];      // sequence rows of the K and V rows this thread stages next
   auto fetch_idx = [&](int tile) {
     const int key = tile * kBN + tid;
     return (IDX && tid < kBN && key < n) ? idx_h[key] : L;
   };
   auto put_idx = [&](int tile, int val) {
-    if (IDX && tid < kBN) idx_s[tile & 1][tid] = val;
+    if (IDX && tid < kBN) idx_s[tile & 3][tid] = val;
   };
   auto read_rows = [&](int tile) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int row = (tid + kThreads * i) / (D / 8);
-      krs[i] = IDX ? idx_s[tile & 1][row] : tile * kBN + row;
+      krs[i] = IDX ? idx_s[tile & 3][row] : tile * kBN + row;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vrs[r] = IDX ? idx_s[tile & 1][4 * vkg + r] : tile * kBN + 4 * vkg + r;
+    for (int r = 0; r < 4; ++r) vrs[r] = IDX ? idx_s[tile & 3][4 * vkg + r] : tile * kBN + 4 * vkg + r;
   };
   auto load_tile = [&](int tile) {
     if (!IDX) read_rows(tile);
@@ -605,19 +606,53 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
       // Tiles t and t+1 sit in buffers t%4 and (t+1)%4; tiles t+2 and t+3
       // are staged into the other two while they are computed, and one
       // barrier per pair publishes them and frees t and t+1.
-      load_tile(0);
-      store_tile(0);
-      if (1 < ntiles) {
-        load_tile(1);
-        store_tile(1);
+      // Indexed: the sequence rows of tile u are fetched from HBM (wave 0)
+      // in the pair two before the one that loads u, published to LDS slot
+      // u % 4 in the pair before it, and read into the row registers half a
+      // pair before the load.
+      int held0 = L, held1 = L;
+      if constexpr (IDX) {
+        const int i0 = fetch_idx(0), i1 = fetch_idx(1), i2 = fetch_idx(2), i3 = fetch_idx(3);
+        const int i4 = fetch_idx(4);
+        held0 = fetch_idx(5);
+        held1 = fetch_idx(6);
+        put_idx(0, i0);
+        put_idx(1, i1);
+        put_idx(2, i2);
+        put_idx(3, i3);
+        __syncthreads();
+        read_rows(0);
+        load_tile(0);
+        store_tile(0);
+        if (1 < ntiles) {
+          read_rows(1);
+          load_tile(1);
+          store_tile(1);
+        }
+        read_rows(2);
+        __syncthreads();                 // slot 0 is free again
+        put_idx(4, i4);
+      } else {
+        load_tile(0);
+        store_tile(0);
+        if (1 < ntiles) {
+          load_tile(1);
+          store_tile(1);
+        }
       }
       __syncthreads();
       for (int t = 0; t < ntiles; t += 2) {
+        put_idx(t + 5, held0);
+        put_idx(t + 6, held1);
+        held0 = fetch_idx(t + 7);        // before the K/V loads: never waits on them
+        held1 = fetch_idx(t + 8);
         if (t + 2 < ntiles) load_tile(t + 2);
+        if (IDX) read_rows(t + 3);
         compute(t, t & 3);
         if (t + 2 < ntiles) store_tile((t + 2) & 3);
         if (t + 1 < ntiles) {
           if (t + 3 < ntiles) load_tile(t + 3);
+          if (IDX) read_rows(t + 4);
           compute(t + 1, (t + 1) & 3);
           if (t + 3 < ntiles) store_tile((t + 3) & 3);
         }
