@@ -30,6 +30,8 @@ INDEXED_CASES = [
     ("bf16", 1, 4, 1, 1500, 64, [1337]),
     ("bf16", 2, 6, 2, 600, 64, [1, 65]),
     ("bf16", 1, 3, 3, 129, 128, [128]),
+    ("bf16", 1, 2, 2, 400, 128, [130]),         # 3 key tiles: a pair and a lone last tile
+    ("bf16", 1, 4, 2, 900, 128, [449]),         # 8 tiles, the last holding one row
     ("f32", 1, 4, 2, 1000, 64, [900]),
     ("f32", 2, 4, 4, 300, 128, [33, 300]),
 ]

@@ -188,6 +188,8 @@ ATTN_CASES = [
     ("bf16", 1, 2, 2, 64, 128, [64], 1),
     ("bf16", 2, 4, 2, 600, 64, None, 2),
     ("bf16", 1, 2, 2, 1500, 64, [1337], 1),
+    ("bf16", 1, 2, 2, 400, 128, [130], 1),      # 3 key tiles: a pair and a lone last tile
+    ("bf16", 1, 2, 2, 600, 64, [449], 1),       # 8 tiles, the last holding one row
     ("f32", 1, 4, 4, 1000, 64, [900], 1),
     ("f32", 1, 4, 2, 300, 128, None, 2),
 ]
