@@ -8,8 +8,9 @@
 //
 // bf16 path (gfx950 MFMA, wave64):
 //   * a workgroup owns 256 query rows of one head (8 waves x 32 rows, two
-//     waves per SIMD) and walks 64-key tiles of K and V, double-buffered in
-//     LDS;
+//     waves per SIMD) and walks 64-key tiles of K and V through four LDS
+//     buffers: two tiles are computed per barrier while the next two are
+//     staged;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the A operand is 32 keys
 //     read from LDS, the B operand is the wave's 32 query rows kept in
 //     registers, so every lane owns one query row;
@@ -116,10 +117,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   constexpr int KS = D / 16;                           // k-steps of S^T
   constexpr int NSUB = kBN / 32;                       // 32-key subtiles
   static_assert(KCH >= 1 && VPAIRS <= kThreads, "tile shape");
-  // Dense and indexed walks: four tile buffers, one barrier per two tiles.
-  // Block-sparse walk: two buffers, one barrier per tile.
-  constexpr int NBUF = BS ? 2 : 4;
-  __shared__ AttnSmem<D, NBUF> sm;
+  // Four tile buffers: the main walks compute two tiles per barrier while
+  // the next two are staged; the exact-max rescans use two of them.
+  __shared__ AttnSmem<D, 4> sm;
   __shared__ int idx_s[IDX ? 4 : 1][kBN];     // sequence rows of upcoming key tiles (slot = tile % 4)
 
   const int tid = threadIdx.x;
@@ -492,9 +492,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   // attempt 0: reference = max of the first key tile; attempt 1 (rare): exact row max.
   for (int attempt = 0; attempt < 2; ++attempt) {
     if constexpr (BS) {
-      // Walk only the tiles the workgroup needs, double-buffered in order.
-      // The next tile, and whether this wave uses it, are looked up one
-      // iteration ahead, so no mask read sits in front of a tile's work.
+      // Walk only the tiles the workgroup needs, in order.  The next tiles,
+      // and whether this wave uses them, are looked up ahead, so no mask
+      // read sits in front of a tile's work.  (The exact-max rescan walks
+      // one tile per barrier through two buffers.)
       if (attempt == 1) {
         float m = -INFINITY;
         int cur = begin_bs(), buf = 0;
@@ -529,39 +530,63 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
       for (int i = 0; i < DT; ++i) oacc[i] = zero;
       l_run = 0.f;
       bool have_ref = attempt == 1;      // the first tile a wave uses sets its reference
-      int cur = begin_bs(), buf = 0;
-      bool use_cur = wave_uses(cur);
-      int nxt = next_from(cur + 1);
-      bool use_nxt = nxt < ntiles && wave_uses(nxt);
-      load_tile(cur);
-      store_tile(0);
-      __syncthreads();
-      while (true) {
-        if (nxt < ntiles) load_tile(nxt);
-        if (use_cur) {
-          if (cur < wdiag && have_ref) {
-            hot(buf);
-          } else {
-            f32x16 sacc[NSUB];
-            qk(buf, sacc, have_ref ? bias : zero);
-            if (cur == wdiag) mask(cur * kBN, sacc);
-            if (!have_ref) set_ref(tile_max(sacc));
-            pv(buf, sacc, have_ref);
-          }
-          have_ref = true;
+      auto bs_compute = [&](int tile, bool use, int buf) {
+        if (!use) return;
+        if (tile < wdiag && have_ref) {
+          hot(buf);
+        } else {
+          f32x16 sacc[NSUB];
+          qk(buf, sacc, have_ref ? bias : zero);
+          if (tile == wdiag) mask(tile * kBN, sacc);
+          if (!have_ref) set_ref(tile_max(sacc));
+          pv(buf, sacc, have_ref);
         }
-        // The walk's bookkeeping for the iteration after next runs while this
-        // tile's last MFMAs drain, not in front of the next tile's work.
-        const int nxt2 = nxt < ntiles ? next_from(nxt + 1) : ntiles;
-        const bool use_nxt2 = nxt2 < ntiles && wave_uses(nxt2);
-        if (nxt < ntiles) store_tile(buf ^ 1);
+        have_ref = true;
+      };
+      // The needed tiles c0 < c1 < c2 < c3 (ntiles when exhausted), with
+      // whether this wave uses each: c0 and c1 sit in buffers s and s+1 and
+      // are computed while c2 and c3 are staged into s+2 and s+3; one
+      // barrier per pair.
+      int c0 = begin_bs();
+      bool u0 = wave_uses(c0);
+      int c1 = c0 < ntiles ? next_from(c0 + 1) : ntiles;
+      bool u1 = c1 < ntiles && wave_uses(c1);
+      int c2 = c1 < ntiles ? next_from(c1 + 1) : ntiles;
+      bool u2 = c2 < ntiles && wave_uses(c2);
+      int c3 = c2 < ntiles ? next_from(c2 + 1) : ntiles;
+      bool u3 = c3 < ntiles && wave_uses(c3);
+      load_tile(c0);
+      store_tile(0);
+      if (c1 < ntiles) {
+        load_tile(c1);
+        store_tile(1);
+      }
+      __syncthreads();
+      int sb0 = 0;
+      while (true) {
+        if (c2 < ntiles) load_tile(c2);
+        bs_compute(c0, u0, sb0);
+        if (c2 < ntiles) store_tile((sb0 + 2) & 3);
+        if (c3 < ntiles) load_tile(c3);
+        if (c1 < ntiles) bs_compute(c1, u1, (sb0 + 1) & 3);
+        // The walk's look-ahead runs while this pair's last MFMAs drain, not
+        // in front of the next pair's work.
+        const int c4 = c3 < ntiles ? next_from(c3 + 1) : ntiles;
+        const bool u4 = c4 < ntiles && wave_uses(c4);
+        const int c5 = c4 < ntiles ? next_from(c4 + 1) : ntiles;
+        const bool u5 = c5 < ntiles && wave_uses(c5);
+        if (c3 < ntiles) store_tile((sb0 + 3) & 3);
         __syncthreads();
-        if (nxt >= ntiles) break;
-        cur = nxt;
-        nxt = nxt2;
-        use_cur = use_nxt;
-        use_nxt = use_nxt2;
-        buf ^= 1;
+        if (c2 >= ntiles) break;
+        c0 = c2;
+        u0 = u2;
+        c1 = c3;
+        u1 = u3;
+        c2 = c4;
+        u2 = u4;
+        c3 = c5;
+        u3 = u5;
+        sb0 = (sb0 + 2) & 3;
       }
       const bool bad = !(sum_halves(l_run) <= kSumLimit);
       if (!__syncthreads_or(bad)) break;
@@ -602,74 +627,60 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
         pv(buf, sacc, !ref_tile);
       }
     };
-    if constexpr (NBUF == 4) {
-      // Tiles t and t+1 sit in buffers t%4 and (t+1)%4; tiles t+2 and t+3
-      // are staged into the other two while they are computed, and one
-      // barrier per pair publishes them and frees t and t+1.
-      // Indexed: the sequence rows of tile u are fetched from HBM (wave 0)
-      // in the pair two before the one that loads u, published to LDS slot
-      // u % 4 in the pair before it, and read into the row registers half a
-      // pair before the load.
-      int held0 = L, held1 = L;
-      if constexpr (IDX) {
-        const int i0 = fetch_idx(0), i1 = fetch_idx(1), i2 = fetch_idx(2), i3 = fetch_idx(3);
-        const int i4 = fetch_idx(4);
-        held0 = fetch_idx(5);
-        held1 = fetch_idx(6);
-        put_idx(0, i0);
-        put_idx(1, i1);
-        put_idx(2, i2);
-        put_idx(3, i3);
-        __syncthreads();
-        read_rows(0);
-        load_tile(0);
-        store_tile(0);
-        if (1 < ntiles) {
-          read_rows(1);
-          load_tile(1);
-          store_tile(1);
-        }
-        read_rows(2);
-        __syncthreads();                 // slot 0 is free again
-        put_idx(4, i4);
-      } else {
-        load_tile(0);
-        store_tile(0);
-        if (1 < ntiles) {
-          load_tile(1);
-          store_tile(1);
-        }
+    // Tiles t and t+1 sit in buffers t%4 and (t+1)%4; tiles t+2 and t+3
+    // are staged into the other two while they are computed, and one
+    // barrier per pair publishes them and frees t and t+1.
+    // Indexed: the sequence rows of tile u are fetched from HBM (wave 0)
+    // in the pair two before the one that loads u, published to LDS slot
+    // u % 4 in the pair before it, and read into the row registers half a
+    // pair before the load.
+    int held0 = L, held1 = L;
+    if constexpr (IDX) {
+      const int i0 = fetch_idx(0), i1 = fetch_idx(1), i2 = fetch_idx(2), i3 = fetch_idx(3);
+      const int i4 = fetch_idx(4);
+      held0 = fetch_idx(5);
+      held1 = fetch_idx(6);
+      put_idx(0, i0);
+      put_idx(1, i1);
+      put_idx(2, i2);
+      put_idx(3, i3);
+      __syncthreads();
+      read_rows(0);
+      load_tile(0);
+      store_tile(0);
+      if (1 < ntiles) {
+        read_rows(1);
+        load_tile(1);
+        store_tile(1);
+      }
+      read_rows(2);
+      __syncthreads();                 // slot 0 is free again
+      put_idx(4, i4);
+    } else {
+      load_tile(0);
+      store_tile(0);
+      if (1 < ntiles) {
+        load_tile(1);
+        store_tile(1);
+      }
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+      put_idx(t + 5, held0);
+      put_idx(t + 6, held1);
+      held0 = fetch_idx(t + 7);        // before the K/V loads: never waits on them
+      held1 = fetch_idx(t + 8);
+      if (t + 2 < ntiles) load_tile(t + 2);
+      if (IDX) read_rows(t + 3);
+      compute(t, t & 3);
+      if (t + 2 < ntiles) store_tile((t + 2) & 3);
+      if (t + 1 < ntiles) {
+        if (t + 3 < ntiles) load_tile(t + 3);
+        if (IDX) read_rows(t + 4);
+        compute(t + 1, (t + 1) & 3);
+        if (t + 3 < ntiles) store_tile((t + 3) & 3);
       }
       __syncthreads();
-      for (int t = 0; t < ntiles; t += 2) {
-        put_idx(t + 5, held0);
-        put_idx(t + 6, held1);
-        held0 = fetch_idx(t + 7);        // before the K/V loads: never waits on them
-        held1 = fetch_idx(t + 8);
-        if (t + 2 < ntiles) load_tile(t + 2);
-        if (IDX) read_rows(t + 3);
-        compute(t, t & 3);
-        if (t + 2 < ntiles) store_tile((t + 2) & 3);
-        if (t + 1 < ntiles) {
-          if (t + 3 < ntiles) load_tile(t + 3);
-          if (IDX) read_rows(t + 4);
-          compute(t + 1, (t + 1) & 3);
-          if (t + 3 < ntiles) store_tile((t + 3) & 3);
-        }
-        __syncthreads();
-      }
-    } else {
-      begin_walk();
-      for (int tile = 0; tile < ntiles; ++tile) {
-        const int buf = tile & 1;
-        put_idx(tile + 3, held);
-        held = fetch_idx(tile + 4);               // before the K/V loads: never waits on them
-        if (tile + 1 < ntiles) load_tile(tile + 1);
-        if (IDX) read_rows(tile + 2);
-        compute(tile, buf);
-        if (tile + 1 < ntiles) store_tile(buf ^ 1);
-        __syncthreads();
-      }
     }
     const bool bad = !(sum_halves(l_run) <= kSumLimit);
     if (!__syncthreads_or(bad)) break;
