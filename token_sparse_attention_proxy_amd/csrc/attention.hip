@@ -185,10 +185,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   // Indexed staging.  The sequence rows of key tile t are fetched from HBM
   // (one per thread of wave 0) well before they are needed, published to
   // LDS slot t % 4 before a barrier, and read into this thread's row
-  // registers before the K/V loads of tile t are issued (per-tile walk:
-  // fetched at the top of iteration t-4, published at t-3, read in t-2,
-  // loaded at the top of t-1; paired walk: see there).  The K/V loads then
-  // wait on nothing, and no index work sits before a barrier.
+  // registers before the K/V loads of tile t are issued (the paired main
+  // walk: see there; the per-tile rescan: fetched at the top of iteration
+  // t-4, published at t-3, read in t-2, loaded at the top of t-1).  The K/V
+  // loads then wait on nothing, and no index work sits before a barrier.
   int krs[KCH], vrs[4];      // sequence rows of the K and V rows this thread stages next
   auto fetch_idx = [&](int tile) {
     const int key = tile * kBN + tid;
