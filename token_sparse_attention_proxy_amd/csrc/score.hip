@@ -247,6 +247,9 @@ __global__ __launch_bounds__(kMThreads) void score_mfma_rowstats(
     const int r = r0 + l32;                 // this lane's proxy row
     const int pos = L - w + r;              // its sequence position
     float m = -INFINITY, z = 0.f;
+    // Not unrolled: the rolled loop needs 68-111 VGPRs, four waves per SIMD
+    // instead of two.
+#pragma unroll 1
     for (int kt = 0; kt < kScoreChunk / 32; ++kt) {
       f32x16 acc;
 #pragma unroll
@@ -321,6 +324,9 @@ __global__ __launch_bounds__(kMThreads) void score_mfma_colsum(
       izrow[v] = st.y;                    // 0 for padding rows: they add nothing
       prow[v] = L - w + rr;
     }
+    // Not unrolled: the rolled loop needs 68-111 VGPRs, four waves per SIMD
+    // instead of two.
+#pragma unroll 1
     for (int kt = 0; kt < kScoreChunk / 32; ++kt) {
       f32x16 acc;
 #pragma unroll
