@@ -30,6 +30,24 @@ constexpr int kSigmaThreads = 256;
 constexpr int kCutThreads = 1024;
 constexpr int kDigitBits = 11;
 constexpr int kBuckets = 1 << kDigitBits;
+constexpr int kPer = 4;                      // sigma values per thread per step of the cut
+constexpr int kStep = kCutThreads * kPer;
+
+// sigma[j0 .. j0 + kPer) (0 past nc); two 16-byte loads when aligned.
+__device__ __forceinline__ void load_vals(const uint64_t* __restrict__ sg, int j0, int nc, bool vec,
+                                          uint64_t (&v)[kPer]) {
+  if (vec && j0 + kPer <= nc) {
+#pragma unroll
+    for (int q = 0; q < kPer; q += 2) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(sg + j0 + q);
+      v[q] = uint64_t(x[0]) | (uint64_t(x[1]) << 32);
+      v[q + 1] = uint64_t(x[2]) | (uint64_t(x[3]) << 32);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) v[q] = j0 + q < nc ? sg[j0 + q] : 0;
+  }
+}
 
 __device__ __forceinline__ uint64_t quantise(float x) {
   // fmaxf/fminf return the non-NaN operand, so NaN counts as 0.
@@ -89,6 +107,7 @@ __global__ __launch_bounds__(kCutThreads) void budget_cut(const uint64_t* __rest
   const int b = blockIdx.x;
   const int t = threadIdx.x;
   const uint64_t* sg = sigma + int64_t(b) * L;
+  const bool vec = (L % 2) == 0 && (reinterpret_cast<uintptr_t>(sigma) % 16) == 0;   // 16-byte rows
   const uint64_t maxv = sigmax[b];
   int lo = maxv ? 64 - __clzll((long long)maxv) : 1;   // bits above `lo` are zero for all values
   uint64_t prefix = 0;          // value of bits [lo + width, 64) shared by the candidates
@@ -107,14 +126,22 @@ __global__ __launch_bounds__(kCutThreads) void budget_cut(const uint64_t* __rest
     }
     if (t == 0) first_cross = kBuckets;
     __syncthreads();
-    for (int j = t; j < nc; j += kCutThreads) {
-      const uint64_t v = sg[j];
-      const uint64_t top = hi >= 64 ? 0 : (v >> hi);
-      if (top == prefix) {
-        const int dgt = int((v >> lo) & uint64_t(kBuckets - 1));
-        atomicAdd(&cnt[dgt], 1u);
-        atomicAdd(reinterpret_cast<unsigned long long*>(&mass[dgt]), (unsigned long long)v);
+    // Four values per thread per step, the next step's loads issued first.
+    uint64_t v[kPer], vn[kPer];
+    load_vals(sg, kPer * t, nc, vec, v);
+    for (int base = 0; base < nc; base += kStep) {
+      load_vals(sg, base + kStep + kPer * t, nc, vec, vn);
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const uint64_t top = hi >= 64 ? 0 : (v[q] >> hi);
+        if (base + kPer * t + q < nc && top == prefix) {
+          const int dgt = int((v[q] >> lo) & uint64_t(kBuckets - 1));
+          atomicAdd(&cnt[dgt], 1u);
+          atomicAdd(reinterpret_cast<unsigned long long*>(&mass[dgt]), (unsigned long long)v[q]);
+        }
       }
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) v[q] = vn[q];
     }
     __syncthreads();
     // Each thread owns two consecutive buckets; exclusive scan of their masses.
