@@ -26,12 +26,14 @@
 //     an accumulator holding -m, so the subtraction costs nothing, and the
 //     loop needs no running max, no cross-lane reduction and no rescaling
 //     of O, which stays in accumulator registers touched only by MFMA: one
-//     exp2, one add and half a bf16 pack per score.  Softmax is invariant
-//     to the reference, so the result equals the usual one up to rounding.
+//     exp2, half a bf16 pack and half a dot2 (the row sum) per score.
+//     Softmax is invariant to the reference, so the result equals the usual
+//     one up to rounding.
 //     A row sum above 2^64 (a later logit far above the first tile's max)
 //     makes the workgroup recompute with the exact row max as reference, so
 //     nothing can overflow;
-//   * P rounded to bf16 for the PV product, fp32 output accumulators, final
+//   * P rounded to bf16 for the PV product, row sums of that rounded P (so
+//     the weights applied to V sum to one), fp32 output accumulators, final
 //     division and round-to-nearest-even to bf16;
 //   * loads and stores go through buffer resources sized to the n valid
 //     rows: out-of-range rows read as 0 and are never written, without
@@ -83,6 +85,13 @@ __device__ __forceinline__ float max_halves(float x) {
 __device__ __forceinline__ float sum_halves(float x) {
   auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// acc + the two bf16 halves of w (one dot2 against (1, 1))
+__device__ __forceinline__ float add_pair(float acc, uint32_t w) {
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, acc, false);
 }
 
 template <int D, int NBUF>
@@ -302,7 +311,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   float l_run = 0.f;      // this lane's share of the row sum
 
   // P = exp2(S - m_ref) (biased: S^T already holds -m_ref from its chain start),
-  // row sums, then O^T += V^T P^T.
+  // rounded to bf16; row sums of the rounded P (a dot2 of each packed pair
+  // against (1, 1)), then O^T += V^T P^T.
   auto pv = [&](int buf, const f32x16 (&sacc)[NSUB], bool biased) {
     const float mneg = biased ? 0.f : -m_ref;
     bf16x8 pb[NSUB * 2];
@@ -316,9 +326,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
         for (int e2 = 0; e2 < 4; ++e2) {
           const float p0 = __builtin_amdgcn_exp2f(sacc[sb][8 * tt + 2 * e2] + mneg);
           const float p1 = __builtin_amdgcn_exp2f(sacc[sb][8 * tt + 2 * e2 + 1] + mneg);
-          ls[(2 * e2) & 3] += p0;
-          ls[(2 * e2 + 1) & 3] += p1;
           pk[e2] = pack_bf16x2(p0, p1);
+          ls[e2] = add_pair(ls[e2], pk[e2]);
         }
         pb[2 * sb + tt] = __builtin_bit_cast(bf16x8, pk);
       }
@@ -336,7 +345,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   // orders, so the same bits) for tiles below the diagonal, written as one
   // software pipeline in program order: LDS operand reads run PF ahead of
   // their MFMA, the S^T chain of subtile q+1 carries the exp/convert work of
-  // subtile q, and the PV MFMAs of the first subtiles carry that of the last.
+  // subtile q, the PV MFMAs of the first subtiles carry that of the last, and
+  // the remaining PV MFMAs carry the row sums.
   auto hot = [&](int buf) {
     constexpr int NQK = NSUB * KS;            // S^T MFMAs, chain after chain
     constexpr int NPV = 2 * NSUB * DT;        // O^T MFMAs, kk-major
@@ -360,8 +370,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     auto softmax_pair = [&](int sb, int p) {  // elements 2p, 2p+1 of subtile sb
       const float p0 = __builtin_amdgcn_exp2f(sacc[sb][2 * p]);
       const float p1 = __builtin_amdgcn_exp2f(sacc[sb][2 * p + 1]);
-      ls[(2 * p) & 3] += p0;
-      ls[(2 * p + 1) & 3] += p1;
       pk[2 * sb + p / 4][p % 4] = pack_bf16x2(p0, p1);
     };
     bf16x8 ring[PF + 1];
@@ -385,18 +393,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
         if (j < LAST_SLOT) {
 #pragma unroll
           for (int p = j * LPP; p < (j + 1) * LPP && p < 8; ++p) softmax_pair(LAST, p);
+        } else {
+          // Row sums of the packed P, in the PV MFMAs that carry no softmax.
+          constexpr int NPK = 8 * NSUB;        // packed words of this tile's P
+          constexpr int SPAN = NPV - LAST_SLOT;
+          constexpr int PER = (NPK + SPAN - 1) / SPAN;
+          const int jj = j - LAST_SLOT;
+#pragma unroll
+          for (int w2 = jj * PER; w2 < (jj + 1) * PER && w2 < NPK; ++w2)
+            ls[w2 & 3] = add_pair(ls[w2 & 3], pk[w2 / 4][w2 % 4]);
         }
       }
     }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    // Pin the operand reads PF MFMAs ahead, whatever the surrounding code.
+    // Pin the operand reads PF MFMAs ahead, whatever the surrounding code,
+    // and spread the tile's 32 exps evenly from a quarter chain after the
+    // first S^T chain ends (its accumulator is then ready), so the row-sum
+    // and pack work fills the gaps between them.
+    constexpr int EXP_PER = 16 / KS;          // exps per MFMA, the rate of the chain that carries them
+    constexpr int EXP_FIRST = KS + KS / 4;
+    constexpr int EXP_SLOTS = 32 / EXP_PER;
+    static_assert(EXP_FIRST + EXP_SLOTS <= NR, "exp slots");
     __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
 #pragma unroll
-    for (int i = 0; i < NR - PF; ++i) {
+    for (int i = 0; i < NR; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i + PF < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i >= EXP_FIRST && i < EXP_FIRST + EXP_SLOTS) __builtin_amdgcn_sched_group_barrier(0x400, EXP_PER, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
   };
 
   // Block mask of this head (BS only).  The workgroup's query blocks are
