@@ -193,3 +193,28 @@ def test_injected_launch_failure_propagates(lib, monkeypatch):
     with pytest.raises(_lib.TsaError) as ei:
         _lib.check(res["forward"], "tsa_forward")
     assert ei.value.name == "TSA_ERR_HIP"
+
+
+def test_last_error_is_per_thread(lib):
+    """Each thread reads back the detail of its own failed call, whatever the others did."""
+    import threading
+    gate = threading.Barrier(2)
+    seen = {}
+
+    def null_problem():
+        lib.tsa_score(None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+        gate.wait()
+        seen["null"] = lib.tsa_last_error().decode()
+
+    def misaligned():
+        lib.tsa_scatter(ctypes.byref(prob()), FAKE + 8, FAKE, FAKE, None)
+        gate.wait()
+        seen["misaligned"] = lib.tsa_last_error().decode()
+
+    threads = [threading.Thread(target=f) for f in (null_problem, misaligned)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert "NULL" in seen["null"] and "aligned" not in seen["null"], seen
+    assert "aligned" in seen["misaligned"] and "NULL" not in seen["misaligned"], seen
