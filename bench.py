@@ -133,7 +133,17 @@ def cpu_baseline(wl, q, k, v, tau, K_gpu: int):
     O.scatter(oc, idx, budget[:1])
     t_scatter = (time.perf_counter() - t0) * B * Hq
     total = t_score + t_budget + t_select + t_gather + t_attn + t_scatter
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    info = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in info] + [1])
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    host = {"cpu_model": cpu_model, "affinity": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count(),
+            "numpy": np.__version__,
+            "blas": sorted({f"{p.get('internal_api')} {p.get('version')}" for p in info if p.get("user_api") == "blas"})}
     return {
         "value": round(total * 1e3, 1), "unit": "ms/layer", "cores": int(threads), "kind": "oracle",
         "sample": (f"fp64 oracle: scores+budget for all {B * Hq} heads in full; select, gather "
@@ -142,6 +152,7 @@ def cpu_baseline(wl, q, k, v, tau, K_gpu: int):
         "measured_s": round(t_score + t_budget + t_select / (B * Hq) + t_gather / (B * Hq)
                             + t_attn_sample + t_scatter / (B * Hq), 2),
         "budget_matches_gpu": bool(int(budget[0]) == K_gpu),
+        "host": host,
     }
 
 
