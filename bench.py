@@ -419,6 +419,13 @@ def main():
                    "GB_s": round(hbm_bytes[n] / (steps_ms[n] * 1e-3) / 1e9, 1),
                    "hbm_frac": round(hbm_bytes[n] / (steps_ms[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                    "algorithmic_bytes": int(hbm_bytes[n])} for n in hbm_bytes}
+    # proxy scoring also runs MFMA work and exps: two passes, each over every (proxy row, key)
+    sc_s = steps_ms["score"] * 1e-3
+    sc_rows = heads * 32 * ((wl.w + 31) // 32)          # proxy rows padded to whole 32-row tiles
+    kernels["score"]["two_pass_tflop"] = round(2 * 2.0 * sc_rows * wl.L * wl.d / 1e12, 4)
+    kernels["score"]["TFLOP_s"] = round(2 * 2.0 * sc_rows * wl.L * wl.d / sc_s / 1e12, 2)
+    kernels["score"]["mfma_frac"] = round(kernels["score"]["TFLOP_s"] / peak, 4) if bf16 else None
+    kernels["score"]["exp_per_s"] = float(f"{2.0 * heads * wl.w * wl.L / sc_s:.4g}")
     for n in ("attention", "attention_indexed"):
         tf = flops / (steps_ms[n] * 1e-3) / 1e12
         kernels[n] = {"ms": round(steps_ms[n], 4), "ms_median": round(float(np.median(per_rep[n])), 4),
