@@ -108,7 +108,7 @@ const char* tsa_version(void);
 size_t tsa_workspace_bytes(const tsa_problem* prob);
 
 /* Scratch bytes needed by tsa_forward: the step scratch plus the
- * intermediate scores, rank map and the four compact per-head tensors. */
+ * intermediate scores, rank map and the compact per-head K and V. */
 size_t tsa_forward_workspace_bytes(const tsa_problem* prob);
 
 /* Scratch bytes needed by tsa_forward_fused: the step scratch plus the
@@ -148,7 +148,8 @@ tsa_status tsa_select(const tsa_problem* prob, const float* s, const int32_t* bu
  *   qc[b,h,i] = Q[b,h,idx_i], kc[b,h,i] = K[b,g(h),idx_i], vc[b,h,i] = V[b,g(h),idx_i].
  * Rows i >= K_b of qc/kc/vc are not written.  q: [B,Hq,L,d]; k, v:
  * [B,Hkv,L,d]; idx: [B,Hq,L] int32 (first K_b entries in [0,L));
- * qc, kc, vc: [B,Hq,L,d] outputs.  Bit-exact copies. */
+ * qc, kc, vc: [B,Hq,L,d] outputs.  Bit-exact copies.  qc may be NULL: then
+ * only kc and vc are written (the input of tsa_attention_qo_indexed). */
 tsa_status tsa_gather(const tsa_problem* prob, const void* q, const void* k, const void* v,
                       const int32_t* idx, const int32_t* budget, void* qc, void* kc, void* vc,
                       void* stream);
@@ -192,10 +193,13 @@ tsa_status tsa_attention_block_sparse(const tsa_problem* prob, const void* q, co
 tsa_status tsa_scatter(const tsa_problem* prob, const void* oc, const int32_t* rank, void* o,
                        void* stream);
 
-/* The whole op: score -> budget -> select -> gather -> attention -> scatter.
- * o: [B,Hq,L,d] output (unselected rows exactly zero); budget: [B] int32
- * output; idx: [B,Hq,L] int32 output (as tsa_select).  ws must hold
- * tsa_forward_workspace_bytes(prob) bytes. */
+/* The whole op: score -> budget -> select -> gather -> attention -> scatter,
+ * run as tsa_score -> tsa_budget -> tsa_select -> tsa_gather of K and V ->
+ * tsa_zero_unselected -> tsa_attention_qo_indexed, which gives the same bits
+ * without materialising the compact Q and O.  o: [B,Hq,L,d] output
+ * (unselected rows exactly zero); budget: [B] int32 output; idx: [B,Hq,L]
+ * int32 output (as tsa_select).  ws must hold tsa_forward_workspace_bytes(prob)
+ * bytes. */
 tsa_status tsa_forward(const tsa_problem* prob, const void* q, const void* k, const void* v,
                        void* o, int32_t* budget, int32_t* idx, void* ws, size_t ws_bytes,
                        void* stream);
@@ -212,6 +216,20 @@ tsa_status tsa_forward(const tsa_problem* prob, const void* q, const void* k, co
 tsa_status tsa_attention_indexed(const tsa_problem* prob, const void* q, const void* k,
                                  const void* v, const int32_t* idx, const int32_t* budget, void* o,
                                  void* stream);
+
+/* Attention of the selected queries over the compressed keys, with Q read and
+ * O written through the index set ("Core architecture", stage 1 attention
+ * and the copy part of stage 2).  For i < K_b, with t = idx[b,h,i]:
+ *   o[b,h,t] = sum_{j<=i} softmax_j(<Q[b,h,t], kc[b,h,j]>/sqrt(d)) vc[b,h,j]
+ * which is tsa_attention(qc, kc, vc, kv_group=1) -> tsa_scatter on the
+ * selected rows, bit for bit, without the compact Q and O.  q, o:
+ * [B,Hq,L,d]; kc, vc: [B,Hq,L,d] as tsa_gather writes them (first K_b rows
+ * valid); idx: [B,Hq,L] int32 as tsa_select writes it; budget: [B] int32
+ * (device), or [B,Hq] under TSA_FLAG_PER_HEAD_BUDGET.  Only the selected
+ * rows of o are written; the other rows are left as they are. */
+tsa_status tsa_attention_qo_indexed(const tsa_problem* prob, const void* q, const void* kc,
+                                    const void* vc, const int32_t* idx, const int32_t* budget,
+                                    void* o, void* stream);
 
 /* Decompression for the fused path ("Core architecture", stage 2, the zero
  * part): o[b,h,j] = +0.0 for every j with rank[b,h,j] < 0; other rows are

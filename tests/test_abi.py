@@ -63,8 +63,9 @@ def test_workspace_sizes(lib):
     step = lib.tsa_workspace_bytes(ctypes.byref(p))
     fwd = lib.tsa_forward_workspace_bytes(ctypes.byref(p))
     assert step > 0 and step % 256 == 0
-    # forward scratch holds at least scores, rank and four compact tensors
-    assert fwd >= step + 4 * 8 * 1000 * 2 + 4 * 8 * 1000 * 128 * 2
+    # forward scratch holds scores, rank and the compact K and V (not Q or O)
+    assert step + 2 * 4 * 8 * 1000 + 2 * 8 * 1000 * 128 * 2 <= fwd
+    assert fwd < step + 2 * 4 * 8 * 1000 + 3 * 8 * 1000 * 128 * 2
     assert lib.tsa_workspace_bytes(ctypes.byref(prob(Hkv=3))) == 0
     assert lib.tsa_workspace_bytes(None) == 0
     # the fused forward needs the step scratch, scores and rank, not the compact tensors
@@ -95,7 +96,7 @@ def test_workspace_scales_with_headline_shape(lib):
     p = prob(Hq=32, Hkv=8, L=131072, w=64)
     fwd = lib.tsa_forward_workspace_bytes(ctypes.byref(p))
     tens = 32 * 131072 * 128 * 2
-    assert 4 * tens < fwd < 4 * tens + 64 * 2 ** 20
+    assert 2 * tens < fwd < 2 * tens + 64 * 2 ** 20
 
 
 BAD_PROBLEMS = [
@@ -129,6 +130,7 @@ def _call_all(lib, p, ptr=FAKE, ws_bytes=1 << 40, kv_group=1):
         "scatter": lib.tsa_scatter(P, ptr, ptr, ptr, None),
         "forward": lib.tsa_forward(P, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ws_bytes, None),
         "attention_indexed": lib.tsa_attention_indexed(P, ptr, ptr, ptr, ptr, ptr, ptr, None),
+        "attention_qo_indexed": lib.tsa_attention_qo_indexed(P, ptr, ptr, ptr, ptr, ptr, ptr, None),
         "forward_fused": lib.tsa_forward_fused(P, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ws_bytes,
                                                None),
         "zero_unselected": lib.tsa_zero_unselected(P, ptr, ptr, None),
@@ -218,3 +220,14 @@ def test_last_error_is_per_thread(lib):
         t.join()
     assert "NULL" in seen["null"] and "aligned" not in seen["null"], seen
     assert "aligned" in seen["misaligned"] and "NULL" not in seen["misaligned"], seen
+
+
+def test_gather_without_q_passes_validation(lib, monkeypatch):
+    """qc = NULL asks for K and V only: validation accepts it (the injected launch failure is
+    what comes back), while a NULL kc is still rejected."""
+    monkeypatch.setenv("TSA_FAULT_INJECT", "launch")
+    P = ctypes.byref(prob())
+    assert lib.tsa_gather(P, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == _lib.TSA_ERR_HIP
+    assert lib.tsa_gather(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == \
+        _lib.TSA_ERR_INVALID_ARG
+    assert "kc" in lib.tsa_last_error().decode()

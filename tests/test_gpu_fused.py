@@ -68,6 +68,38 @@ def test_attention_indexed_equals_steps_and_oracle(case):
     assert_outputs_close(got, ref, dt, what=f" indexed {case}")
 
 
+@pytest.mark.parametrize("case", INDEXED_CASES, ids=[str(c) for c in INDEXED_CASES])
+def test_attention_qo_indexed_equals_steps(case):
+    """Compact K and V, Q read and O written through the index set (the whole op's attention):
+    the same bits as gather -> attention -> scatter on the selected rows, and the K/V-only
+    gather writes the same compact K and V as the full one."""
+    dt, B, Hq, Hkv, L, d, budgets = case
+    say(f"case attention_qo_indexed {case}")
+    q = inputs.make_dense((B, Hq, L, d), 51, dt)
+    k = inputs.make_dense((B, Hkv, L, d), 52, dt, scale=1.5)
+    v = inputs.make_dense((B, Hkv, L, d), 53, dt)
+    budget = np.array(budgets, np.int32)
+    idx, rank = inputs.make_indices(B, Hq, L, budget, seed=54)
+    prob = T.Problem(B, Hq, Hkv, L, d, 1, 0.05, dt)
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    bd = torch.from_numpy(budget).cuda()
+    idd, rkd = torch.from_numpy(idx).cuda(), torch.from_numpy(rank).cuda()
+    qc, kc, vc = T.tsa_gather(prob, qd, kd, vd, idd, bd)
+    oc = T.tsa_attention(prob, qc, kc, vc, bd, 1)
+    o_steps = T.tsa_scatter(prob, oc, rkd)
+    _, kc2, vc2 = T.tsa_gather(prob, qd, kd, vd, idd, bd, with_q=False)
+    o = torch.full((B, Hq, L, d), float("nan"), dtype=qd.dtype, device="cuda")
+    T.tsa_attention_qo_indexed(prob, qd, kc2, vc2, idd, bd, o)
+    torch.cuda.synchronize()
+    for b in range(B):
+        n = int(budget[b])
+        assert torch.equal(_bits(kc2[b, :, :n]), _bits(kc[b, :, :n]))
+        assert torch.equal(_bits(vc2[b, :, :n]), _bits(vc[b, :, :n]))
+    sel = torch.from_numpy(rank >= 0).cuda()
+    assert torch.equal(_bits(o)[sel], _bits(o_steps)[sel])
+    assert torch.isnan(o[~sel].float()).all()
+
+
 @pytest.mark.parametrize("late_key", [700, 130])
 def test_attention_indexed_recompute_path(late_key):
     """Identity index set on inputs that force the exact-max recompute: the

@@ -20,7 +20,7 @@ EXPORTS = ["tsa_status_string", "tsa_last_error", "tsa_version", "tsa_workspace_
            "tsa_forward_workspace_bytes", "tsa_score", "tsa_budget", "tsa_select", "tsa_gather",
            "tsa_attention", "tsa_scatter", "tsa_forward", "tsa_fused_workspace_bytes",
            "tsa_attention_indexed", "tsa_forward_fused", "tsa_zero_unselected",
-           "tsa_block_mask_words", "tsa_attention_block_sparse"]
+           "tsa_block_mask_words", "tsa_attention_block_sparse", "tsa_attention_qo_indexed"]
 
 
 class TsaProblem(ctypes.Structure):
@@ -49,6 +49,7 @@ _SIGNATURES = {
     "tsa_forward": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "tsa_fused_workspace_bytes": (_sz, [_P]),
     "tsa_attention_indexed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "tsa_attention_qo_indexed": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tsa_forward_fused": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "tsa_zero_unselected": (ctypes.c_int, [_P, _vp, _vp, _vp]),
     "tsa_block_mask_words": (_sz, [_P]),

@@ -112,7 +112,10 @@ __device__ __forceinline__ int acc_key(int e, int half) {
 // BS = true: bmask is the block mask, [B*Hq][NB][NW] uint32 with NB = ceil(L/64)
 // and NW = ceil(NB/32); bit kb % 32 of word [qb][kb / 32] set = query block qb
 // sees key block kb.
-template <int D, bool IDX, bool BS>
+// QO = true (with IDX = false): K and V are the compact per-head tensors, and
+// only Q is read and O written through the index set, so the key walk is the
+// compact one and neither a compact Q nor a compact O is needed.
+template <int D, bool IDX, bool BS, bool QO>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ budget,
@@ -155,17 +158,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
 
   // Rows past the valid range read as 0 and are never written.  Indexed
   // reads address the full sequence; compact rows >= n map to row L.
-  const uint32_t head_bytes = uint32_t(IDX ? L : n) * D * 2;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + int64_t(bh) * L * D, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (int64_t(b) * Hk + hk) * L * D, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + (int64_t(b) * Hk + hk) * L * D, head_bytes);
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + int64_t(bh) * L * D, head_bytes);
+  constexpr bool QIDX = IDX || QO;           // Q and O through the index set
+  const uint32_t qo_bytes = uint32_t(QIDX ? L : n) * D * 2;
+  const uint32_t kv_bytes = uint32_t(IDX ? L : n) * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + int64_t(bh) * L * D, qo_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (int64_t(b) * Hk + hk) * L * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + (int64_t(b) * Hk + hk) * L * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + int64_t(bh) * L * D, qo_bytes);
   const int wr0 = q0 + 32 * wave;            // first query row of this wave
   const int qrow = wr0 + l32;                // the row this lane owns
   const int wdiag = wr0 / kBN;               // tile holding this wave's diagonal
 
-  const int32_t* __restrict__ idx_h = IDX ? idx + int64_t(bh) * L : nullptr;
-  const int qsrc = IDX ? (qrow < n ? idx_h[qrow] : L) : qrow;   // sequence row of this lane's query
+  const int32_t* __restrict__ idx_h = QIDX ? idx + int64_t(bh) * L : nullptr;
+  const int qsrc = QIDX ? (qrow < n ? idx_h[qrow] : L) : qrow;   // sequence row of this lane's query
 
   // Q^T as the B operand: lane holds q[qrow][16t + 8*half .. +8].
   bf16x8 qf[KS];
@@ -728,7 +733,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
 constexpr int kF32Rows = 64;    // query rows per workgroup (one per thread)
 constexpr int kF32Keys = 32;    // keys per LDS tile
 
-template <int D, bool IDX, bool BS>
+template <int D, bool IDX, bool BS, bool QO>
 __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ budget, const int32_t* __restrict__ idx,
@@ -748,9 +753,9 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32(
   const int i = q0 + threadIdx.x;
   const int64_t qbase = int64_t(bh) * L * D;
   const int64_t kvbase = (int64_t(b) * Hk + hk) * L * D;
-  const int32_t* __restrict__ idx_h = IDX ? idx + int64_t(bh) * L : nullptr;
+  const int32_t* __restrict__ idx_h = (IDX || QO) ? idx + int64_t(bh) * L : nullptr;
   // sequence row of this query; -1 past the budget (or for an index outside [0, L))
-  int qsrc = i < n ? (IDX ? idx_h[i] : i) : -1;
+  int qsrc = i < n ? ((IDX || QO) ? idx_h[i] : i) : -1;
   if (qsrc >= L) qsrc = -1;
   float qr[D], acc[D];
 #pragma unroll
@@ -810,41 +815,41 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32(
   }
 }
 
-template <int D, bool IDX, bool BS>
+template <int D, bool IDX, bool BS, bool QO>
 hipError_t run_bf16(const Shape& sh, const void* q, const void* k, const void* v,
                     const int32_t* budget, const int32_t* idx, const uint32_t* bmask,
                     int kv_group, void* o, hipStream_t st) {
   const float c = kLog2e / sqrtf(float(D));
   dim3 grid((sh.L + kBM - 1) / kBM, sh.B * sh.Hq);
-  attn_fwd_bf16<D, IDX, BS><<<grid, kThreads, 0, st>>>(
+  attn_fwd_bf16<D, IDX, BS, QO><<<grid, kThreads, 0, st>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), budget, idx, bmask, static_cast<uint16_t*>(o), sh.Hq,
       sh.Hq / kv_group, kv_group, sh.L, sh.bud_b(), sh.bud_h(), c);
   return hipGetLastError();
 }
 
-template <int D, bool IDX, bool BS>
+template <int D, bool IDX, bool BS, bool QO>
 hipError_t run_f32(const Shape& sh, const void* q, const void* k, const void* v,
                    const int32_t* budget, const int32_t* idx, const uint32_t* bmask, int kv_group,
                    void* o, hipStream_t st) {
   const float c = kLog2e / sqrtf(float(D));
   dim3 grid((sh.L + kF32Rows - 1) / kF32Rows, sh.B * sh.Hq);
-  attn_fwd_f32<D, IDX, BS><<<grid, kF32Rows, 0, st>>>(
+  attn_fwd_f32<D, IDX, BS, QO><<<grid, kF32Rows, 0, st>>>(
       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
       budget, idx, bmask, static_cast<float*>(o), sh.Hq, sh.Hq / kv_group, kv_group, sh.L,
       sh.bud_b(), sh.bud_h(), c);
   return hipGetLastError();
 }
 
-template <bool IDX, bool BS>
+template <bool IDX, bool BS, bool QO = false>
 hipError_t run(const Shape& sh, const void* q, const void* k, const void* v,
                const int32_t* budget, const int32_t* idx, const uint32_t* bmask, int kv_group,
                void* o, hipStream_t st) {
   if (sh.dtype == TSA_BF16)
-    return sh.d == 128 ? run_bf16<128, IDX, BS>(sh, q, k, v, budget, idx, bmask, kv_group, o, st)
-                       : run_bf16<64, IDX, BS>(sh, q, k, v, budget, idx, bmask, kv_group, o, st);
-  return sh.d == 128 ? run_f32<128, IDX, BS>(sh, q, k, v, budget, idx, bmask, kv_group, o, st)
-                     : run_f32<64, IDX, BS>(sh, q, k, v, budget, idx, bmask, kv_group, o, st);
+    return sh.d == 128 ? run_bf16<128, IDX, BS, QO>(sh, q, k, v, budget, idx, bmask, kv_group, o, st)
+                       : run_bf16<64, IDX, BS, QO>(sh, q, k, v, budget, idx, bmask, kv_group, o, st);
+  return sh.d == 128 ? run_f32<128, IDX, BS, QO>(sh, q, k, v, budget, idx, bmask, kv_group, o, st)
+                     : run_f32<64, IDX, BS, QO>(sh, q, k, v, budget, idx, bmask, kv_group, o, st);
 }
 
 }  // namespace
@@ -858,6 +863,12 @@ hipError_t launch_attention(const Shape& sh, const void* q, const void* k, const
   }
   return idx ? run<true, false>(sh, q, k, v, budget, idx, nullptr, kv_group, o, st)
              : run<false, false>(sh, q, k, v, budget, nullptr, nullptr, kv_group, o, st);
+}
+
+hipError_t launch_attention_qo(const Shape& sh, const void* q, const void* kc, const void* vc,
+                               const int32_t* budget, const int32_t* idx, void* o,
+                               hipStream_t st) {
+  return run<false, false, true>(sh, q, kc, vc, budget, idx, nullptr, 1, o, st);
 }
 
 }  // namespace tsa

@@ -24,8 +24,9 @@ constexpr int kRowsPerBlock = 64;
 // VPR: 16-byte vectors per row (row bytes / 16).  One block copies compact
 // rows [i0, i0 + kRowsPerBlock) for all G query heads of one KV group, head
 // after head: the heads of a group select nearly the same tokens, so their
-// K/V source rows are read from HBM once and then hit in cache.
-template <int VPR>
+// K/V source rows are read from HBM once and then hit in cache.  WQ = false
+// gathers K and V only (the whole op reads Q through the index set).
+template <int VPR, bool WQ>
 __global__ __launch_bounds__(kThreads) void gather_rows(
     const u32x4* __restrict__ q, const u32x4* __restrict__ k, const u32x4* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ budget, u32x4* __restrict__ qc,
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void gather_rows(
     for (int r = 0; r < R; ++r) {
       const u32x4 z = {0u, 0u, 0u, 0u};
       const bool ok = src[r] >= 0 && src[r] < L;
-      aq[r] = ok ? q[(hrow + src[r]) * VPR + vec] : z;
+      if constexpr (WQ) aq[r] = ok ? q[(hrow + src[r]) * VPR + vec] : z;
       ak[r] = ok ? k[(grow + src[r]) * VPR + vec] : z;
       av[r] = ok ? v[(grow + src[r]) * VPR + vec] : z;
     }
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void gather_rows(
       const int i = i0 + sub + r * kRowsPerPass;
       if (i < i1) {
         const int64_t dst = (hrow + i) * VPR + vec;
-        __builtin_nontemporal_store(aq[r], qc + dst);
+        if constexpr (WQ) __builtin_nontemporal_store(aq[r], qc + dst);
         __builtin_nontemporal_store(ak[r], kc + dst);
         __builtin_nontemporal_store(av[r], vc + dst);
       }
@@ -115,7 +116,8 @@ hipError_t gather_vpr(const Shape& sh, const void* q, const void* k, const void*
                       const int32_t* idx, const int32_t* budget, void* qc, void* kc, void* vc,
                       hipStream_t st) {
   dim3 grid((sh.L + kRowsPerBlock - 1) / kRowsPerBlock, sh.B * sh.Hkv);
-  gather_rows<VPR><<<grid, kThreads, 0, st>>>(
+  auto kern = qc ? gather_rows<VPR, true> : gather_rows<VPR, false>;
+  kern<<<grid, kThreads, 0, st>>>(
       static_cast<const u32x4*>(q), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
       idx, budget, static_cast<u32x4*>(qc), static_cast<u32x4*>(kc), static_cast<u32x4*>(vc),
       sh.Hq, sh.Hkv, sh.L, sh.bud_b(), sh.bud_h());

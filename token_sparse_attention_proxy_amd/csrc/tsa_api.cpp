@@ -128,13 +128,9 @@ FwdWs fwd_ws_layout(const Shape& s) {
   off = align256(off + sizeof(int32_t) * heads * s.L);
   f.fused_total = off;
   const size_t tens = heads * size_t(s.L) * size_t(s.row_bytes());
-  f.qc = off;
-  off = align256(off + tens);
   f.kc = off;
   off = align256(off + tens);
   f.vc = off;
-  off = align256(off + tens);
-  f.oc = off;
   off = align256(off + tens);
   f.total = off;
   return f;
@@ -227,7 +223,7 @@ tsa_status tsa_gather(const tsa_problem* prob, const void* q, const void* k, con
   TSA_TRY(check_ptr(v, "v"));
   TSA_TRY(check_ptr(idx, "idx"));
   TSA_TRY(check_ptr(budget, "budget"));
-  TSA_TRY(check_ptr(qc, "qc"));
+  if (qc) TSA_TRY(check_ptr(qc, "qc"));   // NULL: K and V only
   TSA_TRY(check_ptr(kc, "kc"));
   TSA_TRY(check_ptr(vc, "vc"));
   if (fault_injected()) return injected("tsa_gather");
@@ -306,10 +302,8 @@ tsa_status tsa_forward(const tsa_problem* prob, const void* q, const void* k, co
   hipStream_t st = hipStream_t(stream);
   float* scores = reinterpret_cast<float*>(base + f.scores);
   int32_t* rank = reinterpret_cast<int32_t*>(base + f.rank);
-  void* qc = base + f.qc;
   void* kc = base + f.kc;
   void* vc = base + f.vc;
-  void* oc = base + f.oc;
   hipError_t err;
   if ((err = tsa::launch_score(sh, q, k, scores, base, st)) != hipSuccess)
     return launched(err, "tsa_forward/score");
@@ -317,12 +311,15 @@ tsa_status tsa_forward(const tsa_problem* prob, const void* q, const void* k, co
     return launched(err, "tsa_forward/budget");
   if ((err = tsa::launch_select(sh, scores, budget, idx, rank, base, st)) != hipSuccess)
     return launched(err, "tsa_forward/select");
-  if ((err = tsa::launch_gather(sh, q, k, v, idx, budget, qc, kc, vc, st)) != hipSuccess)
+  // Compression of K and V; the attention reads Q and writes O through the
+  // index set, and the unselected rows are zeroed: the same bits as gather,
+  // attention on the compact Q, K, V and scatter.
+  if ((err = tsa::launch_gather(sh, q, k, v, idx, budget, nullptr, kc, vc, st)) != hipSuccess)
     return launched(err, "tsa_forward/gather");
-  if ((err = tsa::launch_attention(sh, qc, kc, vc, budget, nullptr, 1, oc, st)) != hipSuccess)
+  if ((err = tsa::launch_zero_unselected(sh, rank, o, st)) != hipSuccess)
+    return launched(err, "tsa_forward/zero");
+  if ((err = tsa::launch_attention_qo(sh, q, kc, vc, budget, idx, o, st)) != hipSuccess)
     return launched(err, "tsa_forward/attention");
-  if ((err = tsa::launch_scatter(sh, oc, rank, o, st)) != hipSuccess)
-    return launched(err, "tsa_forward/scatter");
   return ok();
 }
 
@@ -341,6 +338,22 @@ tsa_status tsa_attention_indexed(const tsa_problem* prob, const void* q, const v
   return launched(tsa::launch_attention(sh, q, k, v, budget, idx, sh.Hq / sh.Hkv, o,
                                         hipStream_t(stream)),
                   "tsa_attention_indexed");
+}
+
+tsa_status tsa_attention_qo_indexed(const tsa_problem* prob, const void* q, const void* kc,
+                                    const void* vc, const int32_t* idx, const int32_t* budget,
+                                    void* o, void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_problem(prob, &sh));
+  TSA_TRY(check_ptr(q, "q"));
+  TSA_TRY(check_ptr(kc, "kc"));
+  TSA_TRY(check_ptr(vc, "vc"));
+  TSA_TRY(check_ptr(idx, "idx"));
+  TSA_TRY(check_ptr(budget, "budget"));
+  TSA_TRY(check_ptr(o, "o"));
+  if (fault_injected()) return injected("tsa_attention_qo_indexed");
+  return launched(tsa::launch_attention_qo(sh, q, kc, vc, budget, idx, o, hipStream_t(stream)),
+                  "tsa_attention_qo_indexed");
 }
 
 tsa_status tsa_zero_unselected(const tsa_problem* prob, const int32_t* rank, void* o,

@@ -52,7 +52,7 @@ struct FwdWs {
   size_t scores;      // float [B*Hq*L]
   size_t rank;        // int32 [B*Hq*L]
   size_t fused_total; // end of rank: all the fused forward needs
-  size_t qc, kc, vc, oc;   // dtype [B*Hq*L*d] each
+  size_t kc, vc;      // dtype [B*Hq*L*d] each: compact K and V of every head
   size_t total;
 };
 FwdWs fwd_ws_layout(const Shape& s);
@@ -65,6 +65,7 @@ hipError_t launch_budget(const Shape& s, const float* scores, int32_t* budget, c
                          hipStream_t st);
 hipError_t launch_select(const Shape& s, const float* scores, const int32_t* budget,
                          int32_t* idx, int32_t* rank, char* ws, hipStream_t st);
+// qc == nullptr: K and V only.
 hipError_t launch_gather(const Shape& s, const void* q, const void* k, const void* v,
                          const int32_t* idx, const int32_t* budget, void* qc, void* kc,
                          void* vc, hipStream_t st);
@@ -77,6 +78,11 @@ hipError_t launch_gather(const Shape& s, const void* q, const void* k, const voi
 hipError_t launch_attention(const Shape& s, const void* q, const void* k, const void* v,
                             const int32_t* budget, const int32_t* idx, int kv_group, void* o,
                             hipStream_t st, const uint32_t* bmask = nullptr);
+// K and V compact (kc, vc as launch_gather writes them), Q read and O written
+// through the index set: only the selected rows of o are written.
+hipError_t launch_attention_qo(const Shape& s, const void* q, const void* kc, const void* vc,
+                               const int32_t* budget, const int32_t* idx, void* o,
+                               hipStream_t st);
 hipError_t launch_zero_unselected(const Shape& s, const int32_t* rank, void* o, hipStream_t st);
 hipError_t launch_scatter(const Shape& s, const void* oc, const int32_t* rank, void* o,
                           hipStream_t st);

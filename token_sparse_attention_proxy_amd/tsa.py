@@ -124,16 +124,19 @@ def tsa_select(prob: Problem, s, budget, idx=None, rank=None, ws=None):
     return idx, rank
 
 
-def tsa_gather(prob: Problem, q, k, v, idx, budget, qc=None, kc=None, vc=None):
+def tsa_gather(prob: Problem, q, k, v, idx, budget, qc=None, kc=None, vc=None, with_q=True):
+    """with_q=False gathers K and V only and returns (None, kc, vc)."""
     lib = _lib.load()
     p = prob.c()
     shape = (prob.B, prob.Hq, prob.L, prob.d)
-    qc = _empty(shape, q.dtype, q) if qc is None else qc
+    if with_q:
+        qc = _empty(shape, q.dtype, q) if qc is None else qc
     kc = _empty(shape, q.dtype, q) if kc is None else kc
     vc = _empty(shape, q.dtype, q) if vc is None else vc
     check(lib.tsa_gather(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(budget),
-                         _ptr(qc), _ptr(kc), _ptr(vc), _stream(q.device)), "tsa_gather")
-    return qc, kc, vc
+                         _ptr(qc) if with_q else None, _ptr(kc), _ptr(vc), _stream(q.device)),
+          "tsa_gather")
+    return (qc if with_q else None), kc, vc
 
 
 def tsa_attention(prob: Problem, q, k, v, budget=None, kv_group: int = 1, o=None):
@@ -193,6 +196,17 @@ def tsa_attention_indexed(prob: Problem, q, k, v, idx, budget, o=None):
     check(lib.tsa_attention_indexed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
                                     _ptr(budget), _ptr(o), _stream(q.device)),
           "tsa_attention_indexed")
+    return o
+
+
+def tsa_attention_qo_indexed(prob: Problem, q, kc, vc, idx, budget, o=None):
+    """Writes only the selected rows of o; a new o is zero-filled first."""
+    lib = _lib.load()
+    p = prob.c()
+    o = torch.zeros_like(q) if o is None else o
+    check(lib.tsa_attention_qo_indexed(ctypes.byref(p), _ptr(q), _ptr(kc), _ptr(vc), _ptr(idx),
+                                       _ptr(budget), _ptr(o), _stream(q.device)),
+          "tsa_attention_qo_indexed")
     return o
 
 
