@@ -239,10 +239,12 @@ def main():
         "budget": lambda: T.tsa_budget(prob, s, budget, step_ws),
         "select": lambda: T.tsa_select(prob, s, budget, idx, rank, step_ws),
         "gather": lambda: T.tsa_gather(prob, qd, kd, vd, idx, budget, qc, kc, vc),
+        "gather_kv": lambda: T.tsa_gather(prob, qd, kd, vd, idx, budget, None, kc, vc, with_q=False),
         "attention": lambda: T.tsa_attention(prob, qc, kc, vc, budget, 1, oc),
         "scatter": lambda: T.tsa_scatter(prob, oc, rank, o),
         "zero_fill": lambda: T.tsa_zero_unselected(prob, rank, o),
         "attention_indexed": lambda: T.tsa_attention_indexed(prob, qd, kd, vd, idx, budget, o),
+        "attention_qo": lambda: T.tsa_attention_qo_indexed(prob, qd, kc, vc, idx, budget, o),
     }
     names = list(calls)
     per_rep = {n: [] for n in names}
@@ -385,9 +387,9 @@ def main():
     # ---- roofline of the dominant kernel (the timed path's attention), algorithmic FLOPs
     bf16 = wl.dtype == "bf16"
     flops = attention_flops(bud, wl.Hq, wl.d)
-    attn_step = "attention_indexed" if args.path == "fused" else "attention"
+    attn_step = "attention_indexed" if args.path == "fused" else "attention_qo"
     kname = ("attn_fwd_bf16" if bf16 else "attn_fwd_f32") + \
-        (f"<{wl.d}, true, false>" if args.path == "fused" else f"<{wl.d}, false, false>")
+        (f"<{wl.d}, true, false, false>" if args.path == "fused" else f"<{wl.d}, false, false, true>")
     achieved = flops / (steps_ms[attn_step] * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     traffic = measured_traffic(kname, wl.name) if bf16 else None
@@ -411,6 +413,7 @@ def main():
         "budget": 4 * heads * wl.L,
         "select": 4 * heads * wl.L + 4 * Ksum + 4 * heads * wl.L,
         "gather": Ksum * row + 2 * uniq * row + 3 * Ksum * row + 4 * Ksum,
+        "gather_kv": 2 * uniq * row + 2 * Ksum * row + 4 * Ksum,
         "scatter": Ksum * row + heads * wl.L * row + 4 * heads * wl.L,
         "zero_fill": 4 * heads * wl.L + (heads * wl.L - Ksum) * row,
     }
@@ -426,13 +429,14 @@ def main():
     kernels["score"]["TFLOP_s"] = round(2 * 2.0 * sc_rows * wl.L * wl.d / sc_s / 1e12, 2)
     kernels["score"]["mfma_frac"] = round(kernels["score"]["TFLOP_s"] / peak, 4) if bf16 else None
     kernels["score"]["exp_per_s"] = float(f"{2.0 * heads * wl.w * wl.L / sc_s:.4g}")
-    for n in ("attention", "attention_indexed"):
+    for n in ("attention", "attention_indexed", "attention_qo"):
         tf = flops / (steps_ms[n] * 1e-3) / 1e12
         kernels[n] = {"ms": round(steps_ms[n], 4), "ms_median": round(float(np.median(per_rep[n])), 4),
                       "ms_min": round(float(np.min(per_rep[n])), 4), "TFLOP_s": round(tf, 2),
                       "mfma_frac": round(tf / peak, 4)}
     path_kernels = {"fused": ["score", "budget", "select", "zero_fill", "attention_indexed"],
-                    "steps": ["score", "budget", "select", "gather", "attention", "scatter"]}
+                    "steps": ["score", "budget", "select", "gather_kv", "zero_fill", "attention_qo"],
+                    "entry_points": ["score", "budget", "select", "gather", "attention", "scatter"]}
     overhead = sum(steps_ms[n] for n in path_kernels[args.path] if n != attn_step)
 
     out = {

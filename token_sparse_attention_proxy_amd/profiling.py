@@ -9,7 +9,9 @@ Two sub-commands, meant to run under rocprofv3 and after it:
           workload with its measured budget (random bf16 inputs made on the
           GPU; traffic depends on shapes and the budget, not on values);
         fused: tsa_forward_fused on the workload's own seeded inputs (the
-          indexed attention's reads follow the real index sets).
+          indexed attention's reads follow the real index sets);
+        forward: tsa_forward on the workload's own seeded inputs (its
+          attention reads Q and writes O through the real index sets).
       Run it twice under ``rocprofv3 --pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``.
 
   python -m token_sparse_attention_proxy_amd.profiling summarize \\
@@ -33,6 +35,9 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ATTN_SRC = os.path.join(ROOT, "token_sparse_attention_proxy_amd", "csrc", "attention.hip")
 COPY_BYTES = 1 << 30
+# template arguments (IDX, BS, QO) of the attention kernel each path runs
+KERNEL_ARGS = {"compact": "false, false, false", "fused": "true, false, false",
+               "forward": "false, false, true"}
 
 
 def source_sha(path: str = ATTN_SRC) -> str:
@@ -48,7 +53,7 @@ def cmd_run(args):
 
     wl = inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    if args.path == "fused":
+    if args.path in ("fused", "forward"):
         q, k, v = inputs.make_qkv(wl)
         tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
         qd, kd, vd = (torch.from_numpy(x).to(tdt).to(dev) for x in (q, k, v))
@@ -59,10 +64,11 @@ def cmd_run(args):
     torch.cuda.synchronize()
     del src, dst
     prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, wl.taus[0], wl.dtype)
-    if args.path == "fused":
-        o, bud, _ = T.tsa_forward_fused(prob, qd, kd, vd)
+    if args.path in ("fused", "forward"):
+        run = T.tsa_forward_fused if args.path == "fused" else T.tsa_forward
+        o, bud, _ = run(prob, qd, kd, vd)
         torch.cuda.synchronize()
-        print(f"ran copy of {COPY_BYTES} B and tsa_forward_fused on {wl.name}, "
+        print(f"ran copy of {COPY_BYTES} B and {run.__name__} on {wl.name}, "
               f"budget {bud.cpu().tolist()}")
         return
     g = torch.Generator(device=dev).manual_seed(0)
@@ -101,7 +107,7 @@ def cmd_summarize(args):
     copy_w = max(_pick(write, "copyBuffer")) * 1024.0
     f_scale = COPY_BYTES / copy_f
     w_scale = COPY_BYTES / copy_w
-    kname = f"attn_fwd_bf16<{args.d}, {'true' if args.path == 'fused' else 'false'}, false>"
+    kname = f"attn_fwd_bf16<{args.d}, {KERNEL_ARGS[args.path]}>"
     af = _pick(fetch, kname)
     aw = _pick(write, kname)
     fetch_b = sum(af) / len(af) * 1024.0 * f_scale
@@ -133,14 +139,14 @@ def main():
     r = sub.add_parser("run")
     r.add_argument("--workload", default="llama8b_bf16_L128k")
     r.add_argument("--budget", type=int, default=123997)
-    r.add_argument("--path", choices=["compact", "fused"], default="fused")
+    r.add_argument("--path", choices=sorted(KERNEL_ARGS), default="fused")
     r.set_defaults(fn=cmd_run)
     s = sub.add_parser("summarize")
     s.add_argument("--fetch", required=True)
     s.add_argument("--write", required=True)
     s.add_argument("--workload", default="llama8b_bf16_L128k")
     s.add_argument("--budget", type=int, default=123997)
-    s.add_argument("--path", choices=["compact", "fused"], default="fused")
+    s.add_argument("--path", choices=sorted(KERNEL_ARGS), default="fused")
     s.add_argument("--d", type=int, default=128)
     s.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
     s.set_defaults(fn=cmd_summarize)
