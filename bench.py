@@ -173,7 +173,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the op runs on a single MI355X; see the sharding notes in DESIGN.md)",
+              "(the op runs on a single MI355X; sharding by KV head is a design note only)",
               file=sys.stderr)
         sys.exit(2)
 
