@@ -34,7 +34,7 @@
  *     tensor pointer, any dimension < 1, Hq % Hkv != 0, w > L, Hq > 4096,
  *     L > 2^22, tau outside [0, 1) or NaN, a bad kv_group.
  *     TSA_ERR_UNSUPPORTED: d not in {64, 128}, an unknown dtype, or (bf16)
- *     (Hq/Hkv) * ceil(w/32) > 240 proxy-row tiles per KV head.
+ *     (Hq/Hkv) * ceil(w/32) > 92 proxy-row tiles per KV head.
  *     TSA_ERR_WORKSPACE: ws_bytes below what the *_workspace_bytes query
  *     returns, or a null / misaligned (256 B) workspace.
  *     TSA_ERR_HIP: a launch failed; tsa_last_error() holds the detail.

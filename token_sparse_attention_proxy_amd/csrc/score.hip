@@ -12,9 +12,11 @@
 // Logits are kept in exp2 units: x = <q, k> * log2(e)/sqrt(d).  Every
 // reduction runs in a fixed order, so the result is deterministic.
 //
-// bf16 path (gfx950 MFMA): one workgroup per (128-key chunk, KV head) stages
-// the chunk of K in LDS once and serves all G*w proxy rows of the group's
-// query heads, as 32-row tiles (a head's rows are padded to whole tiles).
+// bf16 path (gfx950 MFMA): each 128-key chunk of a KV head is staged in LDS
+// once and serves all G*w proxy rows of the group's query heads, as 32-row
+// tiles (a head's rows are padded to whole tiles); a workgroup walks a group
+// of consecutive chunks with the next chunk's K loaded while the current one
+// is computed.
 // Pass 1 computes S^T = K Q^T (v_mfma_f32_32x32x16_bf16) so each lane owns a
 // proxy row and keeps an online (max, sum); pass 2 computes S = Q K^T so each
 // lane owns a key column and sums the 16 rows it holds, then the two lane
@@ -179,21 +181,35 @@ __global__ __launch_bounds__(kThreads) void score_pass2(const T* __restrict__ q,
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
-constexpr int kMThreads = 256;          // 4 waves
-constexpr int kMPad = 8;                // bf16 padding per K row in LDS
+constexpr int kMWaves = 8;
+constexpr int kMThreads = 64 * kMWaves;  // 8 waves: one proxy row tile each at the usual shapes
+constexpr int kMPad = 8;                 // bf16 padding per K row in LDS
+constexpr int kMTarget = 512;            // workgroups per pass the chunk grouping aims at
 
-// Stage K rows [j0, j0 + kScoreChunk) of one KV head in LDS (rows past L read as 0).
+// One 128-key chunk of K as 16-byte pieces spread over the workgroup (rows past L read as 0).
 template <int D>
-__device__ __forceinline__ void stage_k_chunk(const uint16_t* __restrict__ kg, int L, int j0,
-                                              uint16_t (*ks)[D + kMPad]) {
-  constexpr int CPR = D / 8;
-  for (int ch = threadIdx.x; ch < kScoreChunk * CPR; ch += kMThreads) {
-    const int row = ch / CPR, col = ch % CPR;
-    u32x4 z = {0u, 0u, 0u, 0u};
-    if (j0 + row < L) z = *reinterpret_cast<const u32x4*>(kg + int64_t(j0 + row) * D + col * 8);
-    *reinterpret_cast<u32x4*>(&ks[row][col * 8]) = z;
+struct KChunk {
+  static constexpr int kCPR = D / 8;                        // pieces per row
+  static constexpr int kN = kScoreChunk * kCPR / kMThreads;  // pieces per thread
+  u32x4 r[kN];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ kg, int L, int j0) {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int ch = threadIdx.x + kMThreads * i;
+      const int row = ch / kCPR, col = ch % kCPR;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (j0 + row < L) z = *reinterpret_cast<const u32x4*>(kg + int64_t(j0 + row) * D + col * 8);
+      r[i] = z;
+    }
   }
-}
+  __device__ __forceinline__ void store(uint16_t (*ks)[D + kMPad]) const {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int ch = threadIdx.x + kMThreads * i;
+      *reinterpret_cast<u32x4*>(&ks[ch / kCPR][(ch % kCPR) * 8]) = r[i];
+    }
+  }
+};
 
 // Q fragments of one 32-row proxy tile: lane holds q[row l%32][16t + 8*(l/32) .. +8];
 // rows past w are zero.
@@ -220,69 +236,91 @@ __device__ __forceinline__ float xhalf_other(float x) {
   return __uint_as_float(lane < 32 ? sw[1] : sw[0]);
 }
 
-// Pass 1: per proxy row, (max, sum of exp2(x - max)) over the chunk's visible keys.
+// Both passes: one workgroup per (group of cpg consecutive 128-key chunks, KV
+// head).  It walks its chunks with K double-buffered in LDS (the next chunk
+// is loaded into registers while the current one is computed), and the proxy
+// row tiles ("units", G * ceil(w/32) of them) are spread over the waves.  When
+// there are no more units than waves, each wave keeps its unit's Q fragments
+// in registers for the whole walk.  The arithmetic per (chunk, unit) is the
+// same as one chunk on its own, so the result does not depend on cpg.
+
+// Pass 1: per proxy row and chunk, (max, sum of exp2(x - max)) over the chunk's visible keys.
 template <int D>
 __global__ __launch_bounds__(kMThreads) void score_mfma_rowstats(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, float2* __restrict__ part,
-    int Hq, int Hkv, int L, int w, int n_chunk, float c, int causal) {
+    int Hq, int Hkv, int L, int w, int n_chunk, int cpg, float c, int causal) {
   constexpr int KS = D / 16;
-  __shared__ uint16_t ks[kScoreChunk][D + kMPad];
-  const int chunk = blockIdx.x, bg = blockIdx.y;
+  __shared__ uint16_t ks[2][kScoreChunk][D + kMPad];
+  const int bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
-  const int G = Hq / Hkv, RT = (w + 31) / 32;
-  const int j0 = chunk * kScoreChunk;
+  const int G = Hq / Hkv, RT = (w + 31) / 32, units = G * RT;
+  const int ch0 = int(blockIdx.x) * cpg, ch1 = min(ch0 + cpg, n_chunk);
+  if (ch0 >= ch1) return;                   // whole workgroup
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l32 = lane & 31, half = lane >> 5;
-  stage_k_chunk<D>(k + (int64_t(b) * Hkv + g) * L * D, L, j0, ks);
+  const uint16_t* kg = k + (int64_t(b) * Hkv + g) * L * D;
+  const bool own = units <= kMWaves;
+  bf16x8 qf[KS];
+  if (own && wave < units)
+    load_q_tile<D>(q + int64_t(b * Hq + g * G + wave / RT) * L * D, L, w, 32 * (wave % RT), qf);
+  KChunk<D> kc;
+  kc.load(kg, L, ch0 * kScoreChunk);
+  kc.store(ks[0]);
   __syncthreads();
-  // keys of this chunk that some proxy row cannot see (causal), or keys past
-  // L (either reading): masking needed
-  const bool edge = causal ? j0 + kScoreChunk - 1 > L - w : j0 + kScoreChunk > L;
   const f32x16 zero = {};
-  for (int unit = wave; unit < G * RT; unit += kMThreads / 64) {
-    const int h = g * G + unit / RT, r0 = 32 * (unit % RT);
-    const int bh = b * Hq + h;
-    bf16x8 qf[KS];
-    load_q_tile<D>(q + int64_t(bh) * L * D, L, w, r0, qf);
-    const int r = r0 + l32;                 // this lane's proxy row
-    const int pos = L - w + r;              // its sequence position
-    float m = -INFINITY, z = 0.f;
-    // Not unrolled: the rolled loop needs 68-111 VGPRs, four waves per SIMD
-    // instead of two.
+  for (int ch = ch0; ch < ch1; ++ch) {
+    const int buf = (ch - ch0) & 1;
+    if (ch + 1 < ch1) kc.load(kg, L, (ch + 1) * kScoreChunk);
+    const int j0 = ch * kScoreChunk;
+    // keys of this chunk that some proxy row cannot see (causal), or keys past
+    // L (either reading): masking needed
+    const bool edge = causal ? j0 + kScoreChunk - 1 > L - w : j0 + kScoreChunk > L;
+    for (int unit = wave; unit < units; unit += kMWaves) {
+      const int h = g * G + unit / RT, r0 = 32 * (unit % RT);
+      const int bh = b * Hq + h;
+      if (!own) load_q_tile<D>(q + int64_t(bh) * L * D, L, w, r0, qf);
+      const int r = r0 + l32;                 // this lane's proxy row
+      const int pos = L - w + r;              // its sequence position
+      float m = -INFINITY, z = 0.f;
+      // Not unrolled: the rolled loop keeps the register count low enough
+      // for two workgroups per CU.
 #pragma unroll 1
-    for (int kt = 0; kt < kScoreChunk / 32; ++kt) {
-      f32x16 acc;
+      for (int kt = 0; kt < kScoreChunk / 32; ++kt) {
+        f32x16 acc;
 #pragma unroll
-      for (int t = 0; t < KS; ++t) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ks[32 * kt + l32][16 * t + 8 * half]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? zero : acc, 0, 0, 0);
+        for (int t = 0; t < KS; ++t) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ks[buf][32 * kt + l32][16 * t + 8 * half]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? zero : acc, 0, 0, 0);
+        }
+        float x[16];
+        float tm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = j0 + 32 * kt + 8 * (e >> 2) + 4 * half + (e & 3);
+          x[e] = acc[e] * c;
+          if (edge && (key > (causal ? pos : L - 1) || r >= w)) x[e] = -INFINITY;
+          tm = fmaxf(tm, x[e]);
+        }
+        const float mn = fmaxf(m, tm);
+        if (mn == -INFINITY) continue;        // nothing visible yet for this lane
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(x[e] - mn);
+        z = z * __builtin_amdgcn_exp2f(m - mn) + sum;
+        m = mn;
       }
-      float x[16];
-      float tm = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = j0 + 32 * kt + 8 * (e >> 2) + 4 * half + (e & 3);
-        x[e] = acc[e] * c;
-        if (edge && (key > (causal ? pos : L - 1) || r >= w)) x[e] = -INFINITY;
-        tm = fmaxf(tm, x[e]);
+      // combine the two lane halves, which saw different keys of the same row
+      const float mo = xhalf_other(m), zo = xhalf_other(z);
+      const float M = fmaxf(m, mo);
+      float Z = 0.f;
+      if (M != -INFINITY) {
+        if (m != -INFINITY) Z += z * __builtin_amdgcn_exp2f(m - M);
+        if (mo != -INFINITY) Z += zo * __builtin_amdgcn_exp2f(mo - M);
       }
-      const float mn = fmaxf(m, tm);
-      if (mn == -INFINITY) continue;        // nothing visible yet for this lane
-      float sum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(x[e] - mn);
-      z = z * __builtin_amdgcn_exp2f(m - mn) + sum;
-      m = mn;
+      if (half == 0 && r < w) part[((int64_t(bh) * w) + r) * n_chunk + ch] = make_float2(M, Z);
     }
-    // combine the two lane halves, which saw different keys of the same row
-    const float mo = xhalf_other(m), zo = xhalf_other(z);
-    const float M = fmaxf(m, mo);
-    float Z = 0.f;
-    if (M != -INFINITY) {
-      if (m != -INFINITY) Z += z * __builtin_amdgcn_exp2f(m - M);
-      if (mo != -INFINITY) Z += zo * __builtin_amdgcn_exp2f(mo - M);
-    }
-    if (half == 0 && r < w) part[((int64_t(bh) * w) + r) * n_chunk + chunk] = make_float2(M, Z);
+    if (ch + 1 < ch1) kc.store(ks[buf ^ 1]);
+    __syncthreads();
   }
 }
 
@@ -291,30 +329,27 @@ template <int D>
 __global__ __launch_bounds__(kMThreads) void score_mfma_colsum(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const float2* __restrict__ rowstat, float* __restrict__ s, int Hq, int Hkv, int L, int w,
-    float c, int causal) {
+    int n_chunk, int cpg, float c, int causal) {
   constexpr int KS = D / 16;
-  extern __shared__ float colsum[];       // [G*RT][kScoreChunk]
-  __shared__ uint16_t ks[kScoreChunk][D + kMPad];
-  const int chunk = blockIdx.x, bg = blockIdx.y;
+  extern __shared__ float colsum[];       // [2][units][kScoreChunk]
+  __shared__ uint16_t ks[2][kScoreChunk][D + kMPad];
+  const int bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
-  const int G = Hq / Hkv, RT = (w + 31) / 32;
-  const int j0 = chunk * kScoreChunk;
+  const int G = Hq / Hkv, RT = (w + 31) / 32, units = G * RT;
+  const int ch0 = int(blockIdx.x) * cpg, ch1 = min(ch0 + cpg, n_chunk);
+  if (ch0 >= ch1) return;                   // whole workgroup
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l32 = lane & 31, half = lane >> 5;
-  stage_k_chunk<D>(k + (int64_t(b) * Hkv + g) * L * D, L, j0, ks);
-  __syncthreads();
-  // causal: keys of this chunk that some proxy row cannot see.  Keys past L
-  // never reach s, so the non-causal reading needs no mask here.
-  const bool edge = causal && j0 + kScoreChunk - 1 > L - w;
-  const f32x16 zero = {};
-  for (int unit = wave; unit < G * RT; unit += kMThreads / 64) {
-    const int h = g * G + unit / RT, r0 = 32 * (unit % RT);
-    const int bh = b * Hq + h;
-    bf16x8 qf[KS];
+  const uint16_t* kg = k + (int64_t(b) * Hkv + g) * L * D;
+  const bool own = units <= kMWaves;
+  // Q fragments and the statistics of the 16 rows this lane holds in the
+  // accumulator, for one unit
+  bf16x8 qf[KS];
+  float mrow[16], izrow[16];
+  int prow[16];
+  auto load_unit = [&](int unit) {
+    const int bh = b * Hq + g * G + unit / RT, r0 = 32 * (unit % RT);
     load_q_tile<D>(q + int64_t(bh) * L * D, L, w, r0, qf);
-    // statistics of the 16 rows this lane holds in the accumulator
-    float mrow[16], izrow[16];
-    int prow[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int rr = r0 + 8 * (v >> 2) + 4 * half + (v & 3);
@@ -324,37 +359,56 @@ __global__ __launch_bounds__(kMThreads) void score_mfma_colsum(
       izrow[v] = st.y;                    // 0 for padding rows: they add nothing
       prow[v] = L - w + rr;
     }
-    // Not unrolled: the rolled loop needs 68-111 VGPRs, four waves per SIMD
-    // instead of two.
-#pragma unroll 1
-    for (int kt = 0; kt < kScoreChunk / 32; ++kt) {
-      f32x16 acc;
-#pragma unroll
-      for (int t = 0; t < KS; ++t) {
-        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&ks[32 * kt + l32][16 * t + 8 * half]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t], bk, t == 0 ? zero : acc, 0, 0, 0);
-      }
-      const int key = j0 + 32 * kt + l32;
-      float cs = 0.f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float p = __builtin_amdgcn_exp2f(fmaf(acc[v], c, -mrow[v])) * izrow[v];
-        if (edge && key > prow[v]) p = 0.f;
-        cs += p;
-      }
-      cs += xhalf_other(cs);
-      if (half == 0) colsum[unit * kScoreChunk + 32 * kt + l32] = cs;
-    }
-  }
+  };
+  if (own && wave < units) load_unit(wave);
+  KChunk<D> kc;
+  kc.load(kg, L, ch0 * kScoreChunk);
+  kc.store(ks[0]);
   __syncthreads();
-  // s = (sum over the head's row tiles, in tile order) / w
-  for (int i = threadIdx.x; i < G * kScoreChunk; i += kMThreads) {
-    const int hl = i / kScoreChunk, kk = i % kScoreChunk;
-    const int j = j0 + kk;
-    if (j >= L) continue;
-    float acc = 0.f;
-    for (int rt = 0; rt < RT; ++rt) acc += colsum[(hl * RT + rt) * kScoreChunk + kk];
-    s[(int64_t(b) * Hq + g * G + hl) * L + j] = acc / float(w);
+  const f32x16 zero = {};
+  for (int ch = ch0; ch < ch1; ++ch) {
+    const int buf = (ch - ch0) & 1;
+    float* cs_buf = colsum + buf * units * kScoreChunk;
+    if (ch + 1 < ch1) kc.load(kg, L, (ch + 1) * kScoreChunk);
+    const int j0 = ch * kScoreChunk;
+    // causal: keys of this chunk that some proxy row cannot see.  Keys past L
+    // never reach s, so the non-causal reading needs no mask here.
+    const bool edge = causal && j0 + kScoreChunk - 1 > L - w;
+    for (int unit = wave; unit < units; unit += kMWaves) {
+      if (!own) load_unit(unit);
+      // Not unrolled: the rolled loop keeps the register count low enough
+      // for two workgroups per CU.
+#pragma unroll 1
+      for (int kt = 0; kt < kScoreChunk / 32; ++kt) {
+        f32x16 acc;
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+          const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&ks[buf][32 * kt + l32][16 * t + 8 * half]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t], bk, t == 0 ? zero : acc, 0, 0, 0);
+        }
+        const int key = j0 + 32 * kt + l32;
+        float csum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float p = __builtin_amdgcn_exp2f(fmaf(acc[v], c, -mrow[v])) * izrow[v];
+          if (edge && key > prow[v]) p = 0.f;
+          csum += p;
+        }
+        csum += xhalf_other(csum);
+        if (half == 0) cs_buf[unit * kScoreChunk + 32 * kt + l32] = csum;
+      }
+    }
+    if (ch + 1 < ch1) kc.store(ks[buf ^ 1]);
+    __syncthreads();
+    // s = (sum over the head's row tiles, in tile order) / w
+    for (int i = threadIdx.x; i < G * kScoreChunk; i += kMThreads) {
+      const int hl = i / kScoreChunk, kk = i % kScoreChunk;
+      const int j = j0 + kk;
+      if (j >= L) continue;
+      float acc = 0.f;
+      for (int rt = 0; rt < RT; ++rt) acc += cs_buf[(hl * RT + rt) * kScoreChunk + kk];
+      s[(int64_t(b) * Hq + g * G + hl) * L + j] = acc / float(w);
+    }
   }
 }
 
@@ -368,17 +422,19 @@ hipError_t run(const Shape& sh, const void* q, const void* k, float* scores, cha
   const int nc = sh.n_chunk();
   const int64_t rows = int64_t(sh.B) * sh.Hq * sh.w;
   if constexpr (std::is_same<T, uint16_t>::value) {
-    const dim3 grid(nc, sh.B * sh.Hkv);
+    const int heads_kv = sh.B * sh.Hkv;
+    const int cpg = max(1, (nc * heads_kv + kMTarget - 1) / kMTarget);   // chunks per workgroup
+    const dim3 grid((nc + cpg - 1) / cpg, heads_kv);
     const int units = sh.G() * ((sh.w + 31) / 32);
-    const size_t colsum_bytes = sizeof(float) * size_t(units) * kScoreChunk;
+    const size_t colsum_bytes = sizeof(float) * 2 * size_t(units) * kScoreChunk;
     score_mfma_rowstats<D><<<grid, kMThreads, 0, st>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), part, sh.Hq, sh.Hkv,
-        sh.L, sh.w, nc, c, int(sh.causal_proxy()));
+        sh.L, sh.w, nc, cpg, c, int(sh.causal_proxy()));
     score_merge<<<unsigned((rows + kMergeWaves - 1) / kMergeWaves), 64 * kMergeWaves, 0, st>>>(
         part, rowstat, rows, nc);
     score_mfma_colsum<D><<<grid, kMThreads, colsum_bytes, st>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), rowstat, scores, sh.Hq,
-        sh.Hkv, sh.L, sh.w, c, int(sh.causal_proxy()));
+        sh.Hkv, sh.L, sh.w, nc, cpg, c, int(sh.causal_proxy()));
   } else {
     const dim3 grid(nc, sh.B * sh.Hq);
     score_pass1<T, D><<<grid, kThreads, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),

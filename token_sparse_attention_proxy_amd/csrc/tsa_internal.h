@@ -12,7 +12,7 @@ namespace tsa {
 // ---------------------------------------------------------------- constants
 constexpr int kScoreFracBits = 50;     // budget masses are counted in units of 2^-50
 constexpr int kScoreChunk = 128;       // keys per proxy-scoring workgroup
-constexpr int kMaxScoreTiles = 240;   // 32-row proxy tiles per KV head (bf16 scoring LDS)
+constexpr int kMaxScoreTiles = 92;    // 32-row proxy tiles per KV head (bf16 scoring LDS)
 constexpr int kMaxHq = 4096;           // keeps the budget's integer masses below 2^63
 constexpr int64_t kMaxL = int64_t(1) << 22;   // per-head tensors stay below 2^31 bytes
 
