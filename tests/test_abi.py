@@ -231,3 +231,18 @@ def test_gather_without_q_passes_validation(lib, monkeypatch):
     assert lib.tsa_gather(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == \
         _lib.TSA_ERR_INVALID_ARG
     assert "kc" in lib.tsa_last_error().decode()
+
+
+def test_score_tile_bound(lib, monkeypatch):
+    """bf16 scoring holds at most 92 proxy-row tiles of 32 rows per KV head in LDS: 92 pass
+    validation (the injected launch failure comes back), 93 are unsupported; fp32 has no bound."""
+    monkeypatch.setenv("TSA_FAULT_INJECT", "launch")
+
+    def score(**kw):
+        p = prob(**kw)
+        return lib.tsa_score(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert score(Hq=2, Hkv=2, L=4096, w=92 * 32) == _lib.TSA_ERR_HIP
+    assert score(Hq=2, Hkv=2, L=4096, w=92 * 32 + 1) == _lib.TSA_ERR_UNSUPPORTED
+    assert score(Hq=4, Hkv=1, L=4096, w=23 * 32) == _lib.TSA_ERR_HIP
+    assert score(Hq=4, Hkv=1, L=4096, w=23 * 32 + 1) == _lib.TSA_ERR_UNSUPPORTED
+    assert score(Hq=2, Hkv=2, L=4096, w=4096, dtype=_lib.TSA_F32) == _lib.TSA_ERR_HIP

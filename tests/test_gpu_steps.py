@@ -30,6 +30,11 @@ SCORE_CASES = [
     inputs.small_workload("f32", B=1, Hq=4, Hkv=2, L=257, d=128, w=20, seed_base=9150),
     inputs.small_workload("bf16", B=1, Hq=4, Hkv=1, L=2048, d=128, w=128, zipf_s=1.1,
                           plant="none", seed_base=9160),
+    # 131 key chunks over 8 KV heads: groups of 3 chunks per workgroup, the last one ragged
+    inputs.small_workload("bf16", B=1, Hq=16, Hkv=8, L=16700, d=128, w=64, seed_base=9170),
+    # the largest bf16 proxy: 92 row tiles of 32 per KV head fill the LDS exactly
+    inputs.small_workload("bf16", B=1, Hq=1, Hkv=1, L=4096, d=128, w=92 * 32, seed_base=9180),
+    inputs.small_workload("bf16", B=1, Hq=2, Hkv=1, L=3000, d=64, w=46 * 32, seed_base=9190),
 ]
 
 
