@@ -19,14 +19,19 @@ namespace tsa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerBlock = 64;
+// Rows per block, measured at the 128K shape: the gather of Q, K and V and the
+// scatter run best with 32, the K/V-only gather and the zero fill with 128.
+constexpr int kRowsGatherQKV = 32;
+constexpr int kRowsGatherKV = 128;
+constexpr int kRowsScatter = 32;
+constexpr int kRowsZero = 128;
 
 // VPR: 16-byte vectors per row (row bytes / 16).  One block copies compact
-// rows [i0, i0 + kRowsPerBlock) for all G query heads of one KV group, head
+// rows [i0, i0 + RPB) for all G query heads of one KV group, head
 // after head: the heads of a group select nearly the same tokens, so their
 // K/V source rows are read from HBM once and then hit in cache.  WQ = false
 // gathers K and V only (the whole op reads Q through the index set).
-template <int VPR, bool WQ>
+template <int VPR, bool WQ, int RPB = WQ ? kRowsGatherQKV : kRowsGatherKV>
 __global__ __launch_bounds__(kThreads) void gather_rows(
     const u32x4* __restrict__ q, const u32x4* __restrict__ k, const u32x4* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ budget, u32x4* __restrict__ qc,
@@ -36,16 +41,16 @@ __global__ __launch_bounds__(kThreads) void gather_rows(
   const int bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
   const int G = Hq / Hkv;
-  const int i0 = blockIdx.x * kRowsPerBlock;
+  const int i0 = blockIdx.x * RPB;
   const int sub = threadIdx.x / VPR, vec = threadIdx.x % VPR;
   const int64_t grow = (int64_t(b) * Hkv + g) * L;        // first row of (b,g)
   for (int hl = 0; hl < G; ++hl) {
     const int h = g * G + hl;
     const int n = min(max(budget[b * bud_b + h * bud_h], 0), L);
     if (i0 >= n) continue;
-    const int i1 = min(i0 + kRowsPerBlock, n);
+    const int i1 = min(i0 + RPB, n);
     const int64_t hrow = (int64_t(b) * Hq + h) * L;   // first row of (b,h)
-    constexpr int R = kRowsPerBlock / kRowsPerPass;   // rows per thread, all loads first
+    constexpr int R = RPB / kRowsPerPass;             // rows per thread, all loads first
     int src[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -80,10 +85,10 @@ __global__ __launch_bounds__(kThreads) void scatter_rows(const u32x4* __restrict
                                                          u32x4* __restrict__ o, int L) {
   constexpr int kRowsPerPass = kThreads / VPR;
   const int bh = blockIdx.y;
-  const int j0 = blockIdx.x * kRowsPerBlock;
+  const int j0 = blockIdx.x * kRowsScatter;
   const int sub = threadIdx.x / VPR, vec = threadIdx.x % VPR;
   const int64_t hrow = int64_t(bh) * L;
-  for (int j = j0 + sub; j < min(j0 + kRowsPerBlock, L); j += kRowsPerPass) {
+  for (int j = j0 + sub; j < min(j0 + kRowsScatter, L); j += kRowsPerPass) {
     const int r = rank[hrow + j];
     u32x4 val = {0u, 0u, 0u, 0u};
     if (r >= 0 && r < L) val = oc[(hrow + r) * VPR + vec];
@@ -96,17 +101,17 @@ __global__ __launch_bounds__(kThreads) void zero_rows(const int32_t* __restrict_
                                                       u32x4* __restrict__ o, int L) {
   constexpr int kRowsPerPass = kThreads / VPR;
   const int bh = blockIdx.y;
-  const int j0 = blockIdx.x * kRowsPerBlock;
+  const int j0 = blockIdx.x * kRowsZero;
   const int sub = threadIdx.x / VPR, vec = threadIdx.x % VPR;
   const int64_t hrow = int64_t(bh) * L;
-  for (int j = j0 + sub; j < min(j0 + kRowsPerBlock, L); j += kRowsPerPass) {
+  for (int j = j0 + sub; j < min(j0 + kRowsZero, L); j += kRowsPerPass) {
     if (rank[hrow + j] < 0) __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, o + (hrow + j) * VPR + vec);
   }
 }
 
 template <int VPR>
 hipError_t zero_vpr(const Shape& sh, const int32_t* rank, void* o, hipStream_t st) {
-  dim3 grid((sh.L + kRowsPerBlock - 1) / kRowsPerBlock, sh.B * sh.Hq);
+  dim3 grid((sh.L + kRowsZero - 1) / kRowsZero, sh.B * sh.Hq);
   zero_rows<VPR><<<grid, kThreads, 0, st>>>(rank, static_cast<u32x4*>(o), sh.L);
   return hipGetLastError();
 }
@@ -115,7 +120,8 @@ template <int VPR>
 hipError_t gather_vpr(const Shape& sh, const void* q, const void* k, const void* v,
                       const int32_t* idx, const int32_t* budget, void* qc, void* kc, void* vc,
                       hipStream_t st) {
-  dim3 grid((sh.L + kRowsPerBlock - 1) / kRowsPerBlock, sh.B * sh.Hkv);
+  const int rpb = qc ? kRowsGatherQKV : kRowsGatherKV;
+  dim3 grid((sh.L + rpb - 1) / rpb, sh.B * sh.Hkv);
   auto kern = qc ? gather_rows<VPR, true> : gather_rows<VPR, false>;
   kern<<<grid, kThreads, 0, st>>>(
       static_cast<const u32x4*>(q), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
@@ -127,7 +133,7 @@ hipError_t gather_vpr(const Shape& sh, const void* q, const void* k, const void*
 template <int VPR>
 hipError_t scatter_vpr(const Shape& sh, const void* oc, const int32_t* rank, void* o,
                        hipStream_t st) {
-  dim3 grid((sh.L + kRowsPerBlock - 1) / kRowsPerBlock, sh.B * sh.Hq);
+  dim3 grid((sh.L + kRowsScatter - 1) / kRowsScatter, sh.B * sh.Hq);
   scatter_rows<VPR><<<grid, kThreads, 0, st>>>(static_cast<const u32x4*>(oc), rank,
                                                 static_cast<u32x4*>(o), sh.L);
   return hipGetLastError();
