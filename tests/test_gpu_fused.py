@@ -144,13 +144,15 @@ def test_forward_fused_small(wl):
     compare_forward(ref, to_np(o), to_np(budget), to_np(idx), q, k, v, tau, wl.dtype)
 
 
-def test_forward_fused_tau0_equals_dense():
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "forward"])
+def test_forward_tau0_equals_dense(fused):
+    """tau = 0 keeps every token: both whole-op paths give the dense kernel's bits."""
     wl = inputs.small_workload("bf16", B=1, Hq=8, Hkv=2, L=1000, d=128, w=64, seed_base=9200)
-    say("case forward_fused tau=0 vs dense")
+    say(f"case tau=0 vs dense, fused={fused}")
     q, k, v = inputs.make_qkv(wl)
     qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
     prob = T.Problem(1, 8, 2, 1000, 128, 64, 0.0, "bf16")
-    o, budget, _ = T.tsa_forward_fused(prob, qd, kd, vd)
+    o, budget, _ = (T.tsa_forward_fused if fused else T.tsa_forward)(prob, qd, kd, vd)
     dense = T.tsa_attention(prob, qd, kd, vd, None, 4)
     torch.cuda.synchronize()
     assert int(budget[0]) == 1000
