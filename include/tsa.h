@@ -231,16 +231,17 @@ tsa_status tsa_attention_qo_indexed(const tsa_problem* prob, const void* q, cons
                                     const void* vc, const int32_t* idx, const int32_t* budget,
                                     void* o, void* stream);
 
-/* Decompression for the fused path ("Core architecture", stage 2, the zero
- * part): o[b,h,j] = +0.0 for every j with rank[b,h,j] < 0; other rows are
+/* Decompression when the attention writes the selected rows itself (the
+ * whole op and the fused path; "Core architecture", stage 2, the zero part): o[b,h,j] = +0.0 for every j with rank[b,h,j] < 0; other rows are
  * left as they are.  rank: [B,Hq,L] int32 (as tsa_select writes it);
  * o: [B,Hq,L,d]. */
 tsa_status tsa_zero_unselected(const tsa_problem* prob, const int32_t* rank, void* o, void* stream);
 
 /* The whole op with the fused kernel: score -> budget -> select ->
  * tsa_zero_unselected -> tsa_attention_indexed.  Same arguments and the
- * same results, bit for bit, as tsa_forward, without the compact tensors:
- * ws must hold tsa_fused_workspace_bytes(prob) bytes. */
+ * same results, bit for bit, as tsa_forward, without the compact K and V
+ * (the attention reads them through the index set): ws must hold
+ * tsa_fused_workspace_bytes(prob) bytes. */
 tsa_status tsa_forward_fused(const tsa_problem* prob, const void* q, const void* k, const void* v,
                              void* o, int32_t* budget, int32_t* idx, void* ws, size_t ws_bytes,
                              void* stream);
