@@ -33,8 +33,9 @@
  *     TSA_ERR_INVALID_ARG: a null problem or tensor pointer, a misaligned
  *     tensor pointer, any dimension < 1, Hq % Hkv != 0, w > L, Hq > 4096,
  *     L > 2^22, tau outside [0, 1) or NaN, a bad kv_group.
- *     TSA_ERR_UNSUPPORTED: d not in {64, 128}, an unknown dtype, or (bf16)
- *     (Hq/Hkv) * ceil(w/32) > 92 proxy-row tiles per KV head.
+ *     TSA_ERR_UNSUPPORTED: d not in {64, 128}, an unknown dtype, B*Hq > 65535
+ *     (sequence-head pairs), or (bf16) w > 2944 (92 proxy-row tiles of 32 rows
+ *     per head).
  *     TSA_ERR_WORKSPACE: ws_bytes below what the *_workspace_bytes query
  *     returns, or a null / misaligned (256 B) workspace.
  *     TSA_ERR_HIP: a launch failed; tsa_last_error() holds the detail.

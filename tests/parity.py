@@ -107,12 +107,14 @@ def _oracle_set(s_row: np.ndarray, K: int, keep: int) -> np.ndarray:
 
 def compare_forward(ref: dict, o_gpu: np.ndarray, budget_gpu: np.ndarray, idx_gpu: np.ndarray,
                     q, k, v, tau: float, dtype: str, sample_rows: int = 0, seed: int = 0,
-                    per_head: bool = False, keep: int = 0):
+                    per_head: bool = False, keep: int = 0, block_heads=(), block_rows: int = 256):
     """End-to-end comparison.  ``ref`` is the oracle's forward() dict (with "o"
     present unless sample_rows > 0, in which case outputs are recomputed for
     sampled rows only).  per_head / keep: the alternative readings (budgets
-    [B,Hq]; the last ``keep`` positions always kept).  Returns a report dict
-    with near-tie counts."""
+    [B,Hq]; the last ``keep`` positions always kept).  block_heads: (b, h)
+    pairs for which, on top of the sampled rows, one random compact row of
+    every block of ``block_rows`` rows (one attention workgroup) is checked.
+    Returns a report dict with near-tie counts."""
     B, Hq, L = idx_gpu.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
@@ -152,6 +154,11 @@ def compare_forward(ref: dict, o_gpu: np.ndarray, budget_gpu: np.ndarray, idx_gp
             assert np.all(o_gpu[b, h, mask] == 0.0)
             if sample_rows:
                 rows = np.unique(np.concatenate([[0, Kg - 1], rng.integers(0, Kg, sample_rows)]))
+                if (b, h) in block_heads:
+                    starts = np.arange(0, Kg, block_rows)
+                    ends = np.minimum(starts + block_rows, Kg)
+                    rows = np.unique(np.concatenate([rows, rng.integers(starts, ends)]))
+                    rep["block_rows_checked"] = rep.get("block_rows_checked", 0) + len(starts)
             else:
                 rows = np.arange(Kg)
             if same and not sample_rows:
@@ -164,5 +171,25 @@ def compare_forward(ref: dict, o_gpu: np.ndarray, budget_gpu: np.ndarray, idx_gp
                                        quiet=True)
             rep["worst_err"] = max(rep["worst_err"], err)
     say(f"[forward] near-ties: budget {rep['budget_near_ties']}, sets {rep['set_near_ties']} "
-        f"of {rep['heads']} heads; worst output err {rep['worst_err']:.3e}")
+        f"of {rep['heads']} heads; worst output err {rep['worst_err']:.3e}"
+        + (f"; {rep['block_rows_checked']} per-block rows" if "block_rows_checked" in rep else ""))
     return rep
+
+
+def check_rows_written(o: torch.Tensor, idx: torch.Tensor, budget: torch.Tensor, per_head=False):
+    """On the device, for an output that was filled with NaN before the call: every selected
+    row is finite (some workgroup wrote it) and every unselected row holds +0.0 bits."""
+    B, Hq, L, _ = o.shape
+    sel = torch.zeros((B, Hq, L), dtype=torch.bool, device=o.device)
+    pos = torch.arange(L, device=o.device)
+    kb = budget.view(B, Hq if per_head else 1).expand(B, Hq).to(torch.int64)
+    valid = pos[None, None, :] < kb[..., None]
+    src = torch.where(valid, idx.to(torch.int64), torch.zeros_like(idx, dtype=torch.int64))
+    sel.scatter_(2, src, valid)
+    bits = o.view(torch.int16 if o.dtype == torch.bfloat16 else torch.int32)
+    n_bad_sel = int((~torch.isfinite(o.float()).all(dim=-1) & sel).sum())
+    n_bad_zero = int(((bits != 0).any(dim=-1) & ~sel).sum())
+    say(f"[rows written] {int(sel.sum())} selected rows finite: {n_bad_sel == 0}; "
+        f"{int((~sel).sum())} unselected rows +0.0: {n_bad_zero == 0}")
+    assert n_bad_sel == 0, f"{n_bad_sel} selected rows were not written"
+    assert n_bad_zero == 0, f"{n_bad_zero} unselected rows are not +0.0"

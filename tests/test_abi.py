@@ -113,7 +113,8 @@ BAD_PROBLEMS = [
     (dict(d=96), _lib.TSA_ERR_UNSUPPORTED),
     (dict(d=256), _lib.TSA_ERR_UNSUPPORTED),
     (dict(dtype=7), _lib.TSA_ERR_UNSUPPORTED),
-    (dict(Hq=64, Hkv=1, w=1000), _lib.TSA_ERR_UNSUPPORTED),
+    (dict(L=4096, w=2945), _lib.TSA_ERR_UNSUPPORTED),
+    (dict(B=16, Hq=4096, Hkv=4096), _lib.TSA_ERR_UNSUPPORTED),     # B*Hq = 65536 > grid y
     (dict(flags=8), _lib.TSA_ERR_UNSUPPORTED),
     (dict(flags=-1), _lib.TSA_ERR_UNSUPPORTED),
 ]
@@ -234,8 +235,9 @@ def test_gather_without_q_passes_validation(lib, monkeypatch):
 
 
 def test_score_tile_bound(lib, monkeypatch):
-    """bf16 scoring holds at most 92 proxy-row tiles of 32 rows per KV head in LDS: 92 pass
-    validation (the injected launch failure comes back), 93 are unsupported; fp32 has no bound."""
+    """bf16 scoring holds at most 92 proxy-row tiles of 32 rows per query head in LDS: 92 pass
+    validation (the injected launch failure comes back), 93 are unsupported, whatever the
+    number of query heads per KV head; fp32 has no bound."""
     monkeypatch.setenv("TSA_FAULT_INJECT", "launch")
 
     def score(**kw):
@@ -243,6 +245,8 @@ def test_score_tile_bound(lib, monkeypatch):
         return lib.tsa_score(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
     assert score(Hq=2, Hkv=2, L=4096, w=92 * 32) == _lib.TSA_ERR_HIP
     assert score(Hq=2, Hkv=2, L=4096, w=92 * 32 + 1) == _lib.TSA_ERR_UNSUPPORTED
-    assert score(Hq=4, Hkv=1, L=4096, w=23 * 32) == _lib.TSA_ERR_HIP
-    assert score(Hq=4, Hkv=1, L=4096, w=23 * 32 + 1) == _lib.TSA_ERR_UNSUPPORTED
+    assert score(Hq=4, Hkv=1, L=4096, w=92 * 32) == _lib.TSA_ERR_HIP
+    assert score(Hq=64, Hkv=1, L=4096, w=64) == _lib.TSA_ERR_HIP         # 128 tiles per KV head
+    assert score(Hq=64, Hkv=1, L=4096, w=92 * 32 + 1) == _lib.TSA_ERR_UNSUPPORTED
+    assert score(Hq=4, Hkv=1, L=4096, w=92 * 32 + 1, dtype=_lib.TSA_F32) == _lib.TSA_ERR_HIP
     assert score(Hq=2, Hkv=2, L=4096, w=4096, dtype=_lib.TSA_F32) == _lib.TSA_ERR_HIP

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from oracle import tsa_oracle as O
-from tests.parity import assert_outputs_close, compare_forward, say, to_dev, to_np
+from tests.parity import assert_outputs_close, check_rows_written, compare_forward, say, to_dev, to_np
 from tests.test_gpu_forward import FULL, SMALL
 from token_sparse_attention_proxy_amd import inputs
 from token_sparse_attention_proxy_amd import tsa as T
@@ -126,6 +126,37 @@ def test_attention_indexed_recompute_path(late_key):
     assert torch.equal(_bits(o), _bits(dense))
 
 
+@pytest.mark.parametrize("late_key", [700, 130])
+def test_attention_qo_recompute_path(late_key):
+    """The whole op's attention (compact K and V, Q read and O written through the index set)
+    on inputs that force the exact-max recompute, with the identity index set: the dense
+    kernel's result bit for bit."""
+    say(f"case attention_qo_indexed recompute late key {late_key}")
+    B, H, L, d = 1, 2, 900, 128
+    rng = np.random.default_rng(78)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = rng.standard_normal((B, H, L, d))
+    k = rng.standard_normal((B, H, L, d))
+    v = rng.standard_normal((B, H, L, d))
+    q[:, :, late_key:] += 10.0 * u
+    k[:, :, late_key] += 60.0 * u
+    prob = T.Problem(B, H, H, L, d, 1, 0.05, "bf16")
+    qd, kd, vd = (to_dev(x.astype(np.float32), "bf16") for x in (q, k, v))
+    idx = torch.arange(L, dtype=torch.int32, device="cuda").repeat(B, H, 1).contiguous()
+    bd = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    o = torch.full_like(qd, float("nan"))
+    T.tsa_attention_qo_indexed(prob, qd, kd, vd, idx, bd, o)
+    dense = T.tsa_attention(prob, qd, kd, vd, None, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o), _bits(dense))
+    # and the oracle, which the recompute must still match
+    qr, kr, vr = (to_np(x) for x in (qd, kd, vd))
+    for h in range(H):
+        ref = O.causal_attention(qr[0, h], kr[0, h], vr[0, h])
+        assert_outputs_close(to_np(o)[0, h], ref, "bf16", what=f" qo recompute h={h}")
+
+
 @pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
 def test_forward_fused_small(wl):
     tau = wl.taus[0]
@@ -170,12 +201,15 @@ def test_forward_fused_full_size(name):
     qd, kd, vd = to_dev(q, wl.dtype), to_dev(k, wl.dtype), to_dev(v, wl.dtype)
     tau = wl.taus[0]
     prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, float(tau), wl.dtype)
-    o, budget, idx = T.tsa_forward_fused(prob, qd, kd, vd)
+    # NaN before the call: a workgroup that never writes its rows cannot pass
+    o = torch.full((wl.B, wl.Hq, wl.L, wl.d), float("nan"), dtype=qd.dtype, device=qd.device)
+    o, budget, idx = T.tsa_forward_fused(prob, qd, kd, vd, o)
     o2, budget2, idx2 = T.tsa_forward(prob, qd, kd, vd)
     torch.cuda.synchronize()
     assert torch.equal(budget, budget2) and torch.equal(idx, idx2)
     assert torch.equal(_bits(o), _bits(o2))
     del o2, budget2, idx2
+    check_rows_written(o, idx, budget)
     say("  oracle scores")
     s_ref = O.proxy_scores(q, k, wl.w)
     b_ref = O.coverage_budget(s_ref, tau)

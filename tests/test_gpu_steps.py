@@ -32,9 +32,14 @@ SCORE_CASES = [
                           plant="none", seed_base=9160),
     # 131 key chunks over 8 KV heads: groups of 3 chunks per workgroup, the last one ragged
     inputs.small_workload("bf16", B=1, Hq=16, Hkv=8, L=16700, d=128, w=64, seed_base=9170),
-    # the largest bf16 proxy: 92 row tiles of 32 per KV head fill the LDS exactly
+    # the largest bf16 proxy: 92 row tiles of 32 per head fill the LDS exactly
     inputs.small_workload("bf16", B=1, Hq=1, Hkv=1, L=4096, d=128, w=92 * 32, seed_base=9180),
     inputs.small_workload("bf16", B=1, Hq=2, Hkv=1, L=3000, d=64, w=46 * 32, seed_base=9190),
+    # more row tiles per KV head than the waves: workgroups take groups of whole heads
+    inputs.small_workload("bf16", B=1, Hq=64, Hkv=1, L=2000, d=128, w=64, seed_base=9191),
+    inputs.small_workload("bf16", B=2, Hq=14, Hkv=2, L=1500, d=128, w=128, seed_base=9192),
+    inputs.small_workload("bf16", B=1, Hq=3, Hkv=1, L=900, d=64, w=96, seed_base=9193),
+    inputs.small_workload("bf16", B=1, Hq=2, Hkv=1, L=3100, d=128, w=92 * 32, seed_base=9194),
 ]
 
 
@@ -264,3 +269,26 @@ def test_attention_recompute_on_large_late_logit(late_key):
         assert_outputs_close(o[0, h], ref, "bf16", what=f" h={h}")
         # rows after the key are dominated by it
         assert np.allclose(ref[late_key + 1:], v[0, h, late_key], atol=1e-3)
+
+
+@pytest.mark.parametrize("logit_std", [4.0, 8.0])
+def test_attention_large_logits(logit_std):
+    """Keys scaled so that the logits q.k/sqrt(d) have standard deviation 4 or 8 (about 2.6
+    and 5 times the Zipf workloads' largest), at L = 8192: the bf16 kernel stays within the
+    2e-2 output tolerance of the fp64 oracle.  Sampled rows span every 256-row workgroup of
+    both heads and the whole range of causal lengths."""
+    say(f"case attention large logits std {logit_std}")
+    B, H, L, d = 1, 2, 8192, 128
+    q = inputs.make_dense((B, H, L, d), 91, "bf16")
+    k = inputs.make_dense((B, H, L, d), 92, "bf16", scale=logit_std)
+    v = inputs.make_dense((B, H, L, d), 93, "bf16")
+    prob = T.Problem(B, H, H, L, d, 1, 0.05, "bf16")
+    o = to_np(T.tsa_attention(prob, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), None, 1))
+    rng = np.random.default_rng(94)
+    starts = np.arange(0, L, 256)
+    rows = np.unique(np.concatenate([rng.integers(starts, starts + 256), [0, 1, L - 1]]))
+    worst = 0.0
+    for h in range(H):
+        ref = O.causal_attention(q[0, h], k[0, h], v[0, h], rows=rows)
+        worst = max(worst, assert_outputs_close(o[0, h, rows], ref, "bf16", what=f" h={h}"))
+    say(f"  logit std {logit_std}: worst rel err {worst:.3e} over {len(rows)} rows per head")

@@ -13,10 +13,10 @@
 // reduction runs in a fixed order, so the result is deterministic.
 //
 // bf16 path (gfx950 MFMA): each 128-key chunk of a KV head is staged in LDS
-// once and serves all G*w proxy rows of the group's query heads, as 32-row
-// tiles (a head's rows are padded to whole tiles); a workgroup walks a group
-// of consecutive chunks with the next chunk's K loaded while the current one
-// is computed.
+// and serves the proxy rows of a group of its query heads (all G of them when
+// their rows fit the eight waves), as 32-row tiles (a head's rows are padded
+// to whole tiles); a workgroup walks a group of consecutive chunks with the
+// next chunk's K loaded while the current one is computed.
 // Pass 1 computes S^T = K Q^T (v_mfma_f32_32x32x16_bf16) so each lane owns a
 // proxy row and keeps an online (max, sum); pass 2 computes S = Q K^T so each
 // lane owns a key column and sums the 16 rows it holds, then the two lane
@@ -186,6 +186,15 @@ constexpr int kMThreads = 64 * kMWaves;  // 8 waves: one proxy row tile each at 
 constexpr int kMPad = 8;                 // bf16 padding per K row in LDS
 constexpr int kMTarget = 512;            // workgroups per pass the chunk grouping aims at
 
+// Query heads of one KV head that a workgroup scores together: all of them
+// when their proxy-row tiles fit the waves, else as many whole heads as fit
+// (at least one).  Each 128-key chunk of K is then staged once per group.
+int score_heads_per_group(int G, int w) {
+  const int rt = (w + 31) / 32;
+  if (G * rt <= kMWaves) return G;
+  return rt >= kMWaves ? 1 : kMWaves / rt;
+}
+
 // One 128-key chunk of K as 16-byte pieces spread over the workgroup (rows past L read as 0).
 template <int D>
 struct KChunk {
@@ -237,23 +246,26 @@ __device__ __forceinline__ float xhalf_other(float x) {
 }
 
 // Both passes: one workgroup per (group of cpg consecutive 128-key chunks, KV
-// head).  It walks its chunks with K double-buffered in LDS (the next chunk
-// is loaded into registers while the current one is computed), and the proxy
-// row tiles ("units", G * ceil(w/32) of them) are spread over the waves.  When
-// there are no more units than waves, each wave keeps its unit's Q fragments
-// in registers for the whole walk.  The arithmetic per (chunk, unit) is the
-// same as one chunk on its own, so the result does not depend on cpg.
+// head, group of hpg of its query heads).  It walks its chunks with K
+// double-buffered in LDS (the next chunk is loaded into registers while the
+// current one is computed), and the proxy row tiles of its heads ("units",
+// ceil(w/32) per head) are spread over the waves.  When there are no more
+// units than waves, each wave keeps its unit's Q fragments in registers for
+// the whole walk.  The arithmetic per (chunk, unit) is the same as one chunk
+// on its own, so the result depends neither on cpg nor on hpg.
 
 // Pass 1: per proxy row and chunk, (max, sum of exp2(x - max)) over the chunk's visible keys.
 template <int D>
 __global__ __launch_bounds__(kMThreads) void score_mfma_rowstats(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, float2* __restrict__ part,
-    int Hq, int Hkv, int L, int w, int n_chunk, int cpg, float c, int causal) {
+    int Hq, int Hkv, int L, int w, int n_chunk, int cpg, int hpg, float c, int causal) {
   constexpr int KS = D / 16;
   __shared__ uint16_t ks[2][kScoreChunk][D + kMPad];
   const int bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
-  const int G = Hq / Hkv, RT = (w + 31) / 32, units = G * RT;
+  const int G = Hq / Hkv, RT = (w + 31) / 32;
+  const int h0 = g * G + int(blockIdx.z) * hpg;            // first query head of this workgroup
+  const int units = min(hpg, g * G + G - h0) * RT;
   const int ch0 = int(blockIdx.x) * cpg, ch1 = min(ch0 + cpg, n_chunk);
   if (ch0 >= ch1) return;                   // whole workgroup
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -262,7 +274,7 @@ __global__ __launch_bounds__(kMThreads) void score_mfma_rowstats(
   const bool own = units <= kMWaves;
   bf16x8 qf[KS];
   if (own && wave < units)
-    load_q_tile<D>(q + int64_t(b * Hq + g * G + wave / RT) * L * D, L, w, 32 * (wave % RT), qf);
+    load_q_tile<D>(q + int64_t(b * Hq + h0 + wave / RT) * L * D, L, w, 32 * (wave % RT), qf);
   KChunk<D> kc;
   kc.load(kg, L, ch0 * kScoreChunk);
   kc.store(ks[0]);
@@ -276,7 +288,7 @@ __global__ __launch_bounds__(kMThreads) void score_mfma_rowstats(
     // L (either reading): masking needed
     const bool edge = causal ? j0 + kScoreChunk - 1 > L - w : j0 + kScoreChunk > L;
     for (int unit = wave; unit < units; unit += kMWaves) {
-      const int h = g * G + unit / RT, r0 = 32 * (unit % RT);
+      const int h = h0 + unit / RT, r0 = 32 * (unit % RT);
       const int bh = b * Hq + h;
       if (!own) load_q_tile<D>(q + int64_t(bh) * L * D, L, w, r0, qf);
       const int r = r0 + l32;                 // this lane's proxy row
@@ -329,13 +341,16 @@ template <int D>
 __global__ __launch_bounds__(kMThreads) void score_mfma_colsum(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const float2* __restrict__ rowstat, float* __restrict__ s, int Hq, int Hkv, int L, int w,
-    int n_chunk, int cpg, float c, int causal) {
+    int n_chunk, int cpg, int hpg, float c, int causal) {
   constexpr int KS = D / 16;
   extern __shared__ float colsum[];       // [2][units][kScoreChunk]
   __shared__ uint16_t ks[2][kScoreChunk][D + kMPad];
   const int bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
-  const int G = Hq / Hkv, RT = (w + 31) / 32, units = G * RT;
+  const int G = Hq / Hkv, RT = (w + 31) / 32;
+  const int h0 = g * G + int(blockIdx.z) * hpg;            // first query head of this workgroup
+  const int nh = min(hpg, g * G + G - h0);                   // its query heads
+  const int units = nh * RT;
   const int ch0 = int(blockIdx.x) * cpg, ch1 = min(ch0 + cpg, n_chunk);
   if (ch0 >= ch1) return;                   // whole workgroup
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -348,7 +363,7 @@ __global__ __launch_bounds__(kMThreads) void score_mfma_colsum(
   float mrow[16], izrow[16];
   int prow[16];
   auto load_unit = [&](int unit) {
-    const int bh = b * Hq + g * G + unit / RT, r0 = 32 * (unit % RT);
+    const int bh = b * Hq + h0 + unit / RT, r0 = 32 * (unit % RT);
     load_q_tile<D>(q + int64_t(bh) * L * D, L, w, r0, qf);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -401,13 +416,13 @@ __global__ __launch_bounds__(kMThreads) void score_mfma_colsum(
     if (ch + 1 < ch1) kc.store(ks[buf ^ 1]);
     __syncthreads();
     // s = (sum over the head's row tiles, in tile order) / w
-    for (int i = threadIdx.x; i < G * kScoreChunk; i += kMThreads) {
+    for (int i = threadIdx.x; i < nh * kScoreChunk; i += kMThreads) {
       const int hl = i / kScoreChunk, kk = i % kScoreChunk;
       const int j = j0 + kk;
       if (j >= L) continue;
       float acc = 0.f;
       for (int rt = 0; rt < RT; ++rt) acc += cs_buf[(hl * RT + rt) * kScoreChunk + kk];
-      s[(int64_t(b) * Hq + g * G + hl) * L + j] = acc / float(w);
+      s[(int64_t(b) * Hq + h0 + hl) * L + j] = acc / float(w);
     }
   }
 }
@@ -423,18 +438,20 @@ hipError_t run(const Shape& sh, const void* q, const void* k, float* scores, cha
   const int64_t rows = int64_t(sh.B) * sh.Hq * sh.w;
   if constexpr (std::is_same<T, uint16_t>::value) {
     const int heads_kv = sh.B * sh.Hkv;
-    const int cpg = max(1, (nc * heads_kv + kMTarget - 1) / kMTarget);   // chunks per workgroup
-    const dim3 grid((nc + cpg - 1) / cpg, heads_kv);
-    const int units = sh.G() * ((sh.w + 31) / 32);
+    const int hpg = score_heads_per_group(sh.G(), sh.w);
+    const int ngroups = (sh.G() + hpg - 1) / hpg;
+    const int cpg = max(1, (nc * heads_kv * ngroups + kMTarget - 1) / kMTarget);   // chunks per workgroup
+    const dim3 grid((nc + cpg - 1) / cpg, heads_kv, ngroups);
+    const int units = hpg * ((sh.w + 31) / 32);
     const size_t colsum_bytes = sizeof(float) * 2 * size_t(units) * kScoreChunk;
     score_mfma_rowstats<D><<<grid, kMThreads, 0, st>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), part, sh.Hq, sh.Hkv,
-        sh.L, sh.w, nc, cpg, c, int(sh.causal_proxy()));
+        sh.L, sh.w, nc, cpg, hpg, c, int(sh.causal_proxy()));
     score_merge<<<unsigned((rows + kMergeWaves - 1) / kMergeWaves), 64 * kMergeWaves, 0, st>>>(
         part, rowstat, rows, nc);
     score_mfma_colsum<D><<<grid, kMThreads, colsum_bytes, st>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), rowstat, scores, sh.Hq,
-        sh.Hkv, sh.L, sh.w, nc, cpg, c, int(sh.causal_proxy()));
+        sh.Hkv, sh.L, sh.w, nc, cpg, hpg, c, int(sh.causal_proxy()));
   } else {
     const dim3 grid(nc, sh.B * sh.Hq);
     score_pass1<T, D><<<grid, kThreads, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),

@@ -45,6 +45,10 @@ tsa_status check_problem(const tsa_problem* p, tsa::Shape* out) {
   if (p->w > p->L) return fail(TSA_ERR_INVALID_ARG, "w=%d exceeds L=%d", p->w, p->L);
   if (p->Hq > tsa::kMaxHq) return fail(TSA_ERR_INVALID_ARG, "Hq=%d exceeds %d", p->Hq, tsa::kMaxHq);
   if (int64_t(p->L) > tsa::kMaxL) return fail(TSA_ERR_INVALID_ARG, "L=%d exceeds 2^22", p->L);
+  // Several launches put the (sequence, head) pair in grid y, whose limit is 65535.
+  if (int64_t(p->B) * p->Hq > tsa::kMaxHeads)
+    return fail(TSA_ERR_UNSUPPORTED, "B*Hq=%lld exceeds %d", (long long)(int64_t(p->B) * p->Hq),
+                tsa::kMaxHeads);
   if (std::isnan(p->tau) || !(p->tau >= 0.0f) || !(p->tau < 1.0f))
     return fail(TSA_ERR_INVALID_ARG, "tau=%g is outside [0, 1)", double(p->tau));
   if (p->flags & ~(TSA_FLAG_NONCAUSAL_PROXY | TSA_FLAG_PER_HEAD_BUDGET | TSA_FLAG_KEEP_WINDOW))
@@ -53,10 +57,9 @@ tsa_status check_problem(const tsa_problem* p, tsa::Shape* out) {
     return fail(TSA_ERR_UNSUPPORTED, "dtype %d is not supported (TSA_F32=0, TSA_BF16=1)", p->dtype);
   if (p->d != 64 && p->d != 128)
     return fail(TSA_ERR_UNSUPPORTED, "head dim d=%d is not supported (64 or 128)", p->d);
-  if (p->dtype == TSA_BF16 && (p->Hq / p->Hkv) * ((p->w + 31) / 32) > tsa::kMaxScoreTiles)
-    return fail(TSA_ERR_UNSUPPORTED,
-                "(Hq/Hkv) * ceil(w/32) = %d proxy-row tiles per KV head exceeds %d",
-                (p->Hq / p->Hkv) * ((p->w + 31) / 32), tsa::kMaxScoreTiles);
+  if (p->dtype == TSA_BF16 && (p->w + 31) / 32 > tsa::kMaxScoreTiles)
+    return fail(TSA_ERR_UNSUPPORTED, "ceil(w/32) = %d proxy-row tiles per head exceeds %d (w <= %d)",
+                (p->w + 31) / 32, tsa::kMaxScoreTiles, 32 * tsa::kMaxScoreTiles);
   *out = tsa::Shape{p->B, p->Hq, p->Hkv, p->L, p->d, p->w, p->tau, p->dtype, p->flags};
   return TSA_OK;
 }

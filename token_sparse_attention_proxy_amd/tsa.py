@@ -64,6 +64,39 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _expect(name: str, t: Optional[torch.Tensor], shape: tuple, dtype: torch.dtype) -> None:
+    """Raise ValueError unless t has exactly this shape and dtype (the kernels read and write
+    whole tensors of the size the problem implies, so a smaller one would be overrun)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected shape {tuple(shape)} and dtype {dtype}, "
+                         f"got {tuple(t.shape)} and {t.dtype}")
+
+
+def _heads(prob: "Problem", n_heads: int) -> tuple:
+    return (prob.B, n_heads, prob.L, prob.d)
+
+
+def _check_qkv(prob: "Problem", q, k, v, kv_heads: int) -> None:
+    dt = prob.torch_dtype
+    _expect("q", q, _heads(prob, prob.Hq), dt)
+    _expect("k", k, _heads(prob, kv_heads), dt)
+    _expect("v", v, _heads(prob, kv_heads), dt)
+
+
+def _check_rows(prob: "Problem", **tensors) -> None:
+    """[B,Hq,L] int32 index and rank maps."""
+    for name, t in tensors.items():
+        _expect(name, t, (prob.B, prob.Hq, prob.L), torch.int32)
+
+
+def _check_budget(prob: "Problem", budget, optional: bool = False) -> None:
+    if budget is None and optional:
+        return
+    _expect("budget", budget, prob.budget_shape, torch.int32)
+
+
 def _stream(dev: torch.device) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
@@ -87,6 +120,8 @@ def fused_workspace_bytes(prob: Problem) -> int:
 def _ws(prob: Problem, like: torch.Tensor, ws: Optional[torch.Tensor], nbytes: int) -> torch.Tensor:
     if ws is None:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=like.device)
+    elif ws.dtype != torch.uint8:
+        raise ValueError(f"ws must be a uint8 byte buffer, got {ws.dtype}")
     return ws
 
 
@@ -95,6 +130,9 @@ def tsa_score(prob: Problem, q, k, s=None, ws=None):
     p = prob.c()
     if s is None:
         s = _empty((prob.B, prob.Hq, prob.L), torch.float32, q)
+    _expect("q", q, _heads(prob, prob.Hq), prob.torch_dtype)
+    _expect("k", k, _heads(prob, prob.Hkv), prob.torch_dtype)
+    _expect("s", s, (prob.B, prob.Hq, prob.L), torch.float32)
     ws = _ws(prob, q, ws, workspace_bytes(prob))
     check(lib.tsa_score(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(s), _ptr(ws), ws.numel(),
                         _stream(q.device)), "tsa_score")
@@ -106,6 +144,8 @@ def tsa_budget(prob: Problem, s, budget=None, ws=None):
     p = prob.c()
     if budget is None:
         budget = _empty(prob.budget_shape, torch.int32, s)
+    _expect("s", s, (prob.B, prob.Hq, prob.L), torch.float32)
+    _check_budget(prob, budget)
     ws = _ws(prob, s, ws, workspace_bytes(prob))
     check(lib.tsa_budget(ctypes.byref(p), _ptr(s), _ptr(budget), _ptr(ws), ws.numel(),
                          _stream(s.device)), "tsa_budget")
@@ -118,6 +158,9 @@ def tsa_select(prob: Problem, s, budget, idx=None, rank=None, ws=None):
     shape = (prob.B, prob.Hq, prob.L)
     idx = _empty(shape, torch.int32, s) if idx is None else idx
     rank = _empty(shape, torch.int32, s) if rank is None else rank
+    _expect("s", s, shape, torch.float32)
+    _check_budget(prob, budget)
+    _check_rows(prob, idx=idx, rank=rank)
     ws = _ws(prob, s, ws, workspace_bytes(prob))
     check(lib.tsa_select(ctypes.byref(p), _ptr(s), _ptr(budget), _ptr(idx), _ptr(rank), _ptr(ws),
                          ws.numel(), _stream(s.device)), "tsa_select")
@@ -133,6 +176,13 @@ def tsa_gather(prob: Problem, q, k, v, idx, budget, qc=None, kc=None, vc=None, w
         qc = _empty(shape, q.dtype, q) if qc is None else qc
     kc = _empty(shape, q.dtype, q) if kc is None else kc
     vc = _empty(shape, q.dtype, q) if vc is None else vc
+    _check_qkv(prob, q, k, v, prob.Hkv)
+    _check_rows(prob, idx=idx)
+    _check_budget(prob, budget)
+    if with_q:
+        _expect("qc", qc, shape, prob.torch_dtype)
+    _expect("kc", kc, shape, prob.torch_dtype)
+    _expect("vc", vc, shape, prob.torch_dtype)
     check(lib.tsa_gather(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(budget),
                          _ptr(qc) if with_q else None, _ptr(kc), _ptr(vc), _stream(q.device)),
           "tsa_gather")
@@ -142,7 +192,12 @@ def tsa_gather(prob: Problem, q, k, v, idx, budget, qc=None, kc=None, vc=None, w
 def tsa_attention(prob: Problem, q, k, v, budget=None, kv_group: int = 1, o=None):
     lib = _lib.load()
     p = prob.c()
+    if kv_group < 1 or prob.Hq % kv_group:
+        raise ValueError(f"kv_group={kv_group} must divide Hq={prob.Hq}")
     o = _empty(q.shape, q.dtype, q) if o is None else o
+    _check_qkv(prob, q, k, v, prob.Hq // kv_group)
+    _expect("o", o, _heads(prob, prob.Hq), prob.torch_dtype)
+    _check_budget(prob, budget, optional=True)
     check(lib.tsa_attention(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(budget), kv_group,
                             _ptr(o), _stream(q.device)), "tsa_attention")
     return o
@@ -160,7 +215,12 @@ def tsa_attention_block_sparse(prob: Problem, q, k, v, block_mask, budget=None, 
     p = prob.c()
     if block_mask.numel() != block_mask_words(prob) or block_mask.element_size() != 4:
         raise ValueError("block_mask must hold block_mask_words(prob) 32-bit words")
+    if kv_group < 1 or prob.Hq % kv_group:
+        raise ValueError(f"kv_group={kv_group} must divide Hq={prob.Hq}")
     o = _empty(q.shape, q.dtype, q) if o is None else o
+    _check_qkv(prob, q, k, v, prob.Hq // kv_group)
+    _expect("o", o, _heads(prob, prob.Hq), prob.torch_dtype)
+    _check_budget(prob, budget, optional=True)
     check(lib.tsa_attention_block_sparse(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(budget),
                                          kv_group, _ptr(block_mask), _ptr(o), _stream(q.device)),
           "tsa_attention_block_sparse")
@@ -171,9 +231,19 @@ def tsa_scatter(prob: Problem, oc, rank, o=None):
     lib = _lib.load()
     p = prob.c()
     o = _empty(oc.shape, oc.dtype, oc) if o is None else o
+    _expect("oc", oc, _heads(prob, prob.Hq), prob.torch_dtype)
+    _expect("o", o, _heads(prob, prob.Hq), prob.torch_dtype)
+    _check_rows(prob, rank=rank)
     check(lib.tsa_scatter(ctypes.byref(p), _ptr(oc), _ptr(rank), _ptr(o), _stream(oc.device)),
           "tsa_scatter")
     return o
+
+
+def _check_forward(prob: Problem, q, k, v, o, budget, idx) -> None:
+    _check_qkv(prob, q, k, v, prob.Hkv)
+    _expect("o", o, _heads(prob, prob.Hq), prob.torch_dtype)
+    _check_budget(prob, budget)
+    _check_rows(prob, idx=idx)
 
 
 def tsa_forward(prob: Problem, q, k, v, o=None, budget=None, idx=None, ws=None):
@@ -182,6 +252,7 @@ def tsa_forward(prob: Problem, q, k, v, o=None, budget=None, idx=None, ws=None):
     o = _empty(q.shape, q.dtype, q) if o is None else o
     budget = _empty(prob.budget_shape, torch.int32, q) if budget is None else budget
     idx = _empty((prob.B, prob.Hq, prob.L), torch.int32, q) if idx is None else idx
+    _check_forward(prob, q, k, v, o, budget, idx)
     ws = _ws(prob, q, ws, forward_workspace_bytes(prob))
     check(lib.tsa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(budget),
                           _ptr(idx), _ptr(ws), ws.numel(), _stream(q.device)), "tsa_forward")
@@ -193,6 +264,10 @@ def tsa_attention_indexed(prob: Problem, q, k, v, idx, budget, o=None):
     lib = _lib.load()
     p = prob.c()
     o = torch.zeros_like(q) if o is None else o
+    _check_qkv(prob, q, k, v, prob.Hkv)
+    _expect("o", o, _heads(prob, prob.Hq), prob.torch_dtype)
+    _check_rows(prob, idx=idx)
+    _check_budget(prob, budget)
     check(lib.tsa_attention_indexed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
                                     _ptr(budget), _ptr(o), _stream(q.device)),
           "tsa_attention_indexed")
@@ -204,6 +279,10 @@ def tsa_attention_qo_indexed(prob: Problem, q, kc, vc, idx, budget, o=None):
     lib = _lib.load()
     p = prob.c()
     o = torch.zeros_like(q) if o is None else o
+    _check_qkv(prob, q, kc, vc, prob.Hq)
+    _expect("o", o, _heads(prob, prob.Hq), prob.torch_dtype)
+    _check_rows(prob, idx=idx)
+    _check_budget(prob, budget)
     check(lib.tsa_attention_qo_indexed(ctypes.byref(p), _ptr(q), _ptr(kc), _ptr(vc), _ptr(idx),
                                        _ptr(budget), _ptr(o), _stream(q.device)),
           "tsa_attention_qo_indexed")
@@ -213,6 +292,8 @@ def tsa_attention_qo_indexed(prob: Problem, q, kc, vc, idx, budget, o=None):
 def tsa_zero_unselected(prob: Problem, rank, o):
     lib = _lib.load()
     p = prob.c()
+    _check_rows(prob, rank=rank)
+    _expect("o", o, _heads(prob, prob.Hq), prob.torch_dtype)
     check(lib.tsa_zero_unselected(ctypes.byref(p), _ptr(rank), _ptr(o), _stream(o.device)),
           "tsa_zero_unselected")
     return o
@@ -224,6 +305,7 @@ def tsa_forward_fused(prob: Problem, q, k, v, o=None, budget=None, idx=None, ws=
     o = _empty(q.shape, q.dtype, q) if o is None else o
     budget = _empty(prob.budget_shape, torch.int32, q) if budget is None else budget
     idx = _empty((prob.B, prob.Hq, prob.L), torch.int32, q) if idx is None else idx
+    _check_forward(prob, q, k, v, o, budget, idx)
     ws = _ws(prob, q, ws, fused_workspace_bytes(prob))
     check(lib.tsa_forward_fused(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                 _ptr(budget), _ptr(idx), _ptr(ws), ws.numel(),
