@@ -180,12 +180,14 @@ def check_rows_written(o: torch.Tensor, idx: torch.Tensor, budget: torch.Tensor,
     """On the device, for an output that was filled with NaN before the call: every selected
     row is finite (some workgroup wrote it) and every unselected row holds +0.0 bits."""
     B, Hq, L, _ = o.shape
-    sel = torch.zeros((B, Hq, L), dtype=torch.bool, device=o.device)
     pos = torch.arange(L, device=o.device)
     kb = budget.view(B, Hq if per_head else 1).expand(B, Hq).to(torch.int64)
     valid = pos[None, None, :] < kb[..., None]
-    src = torch.where(valid, idx.to(torch.int64), torch.zeros_like(idx, dtype=torch.int64))
-    sel.scatter_(2, src, valid)
+    # entries past the budget go to a sentinel column L, dropped afterwards
+    src = torch.where(valid, idx.to(torch.int64), torch.full_like(idx, L, dtype=torch.int64))
+    sel = torch.zeros((B, Hq, L + 1), dtype=torch.bool, device=o.device)
+    sel.scatter_(2, src, torch.ones_like(valid))
+    sel = sel[..., :L]
     bits = o.view(torch.int16 if o.dtype == torch.bfloat16 else torch.int32)
     n_bad_sel = int((~torch.isfinite(o.float()).all(dim=-1) & sel).sum())
     n_bad_zero = int(((bits != 0).any(dim=-1) & ~sel).sum())
