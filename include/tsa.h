@@ -247,6 +247,31 @@ tsa_status tsa_forward_fused(const tsa_problem* prob, const void* q, const void*
                              void* o, int32_t* budget, int32_t* idx, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* Bytes of the library-owned scratch of tsa_forward_fused_noalloc: one copy
+ * per GPU the library runs on, held until the process ends. */
+#define TSA_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * op, arguments and results (bit for bit) as tsa_forward_fused, with the
+ * scratch taken from a static device array of TSA_NOALLOC_SCRATCH_BYTES
+ * instead of a caller workspace.  Nothing is allocated: no hipMalloc,
+ * hipFree or allocating library call.  The caller still passes every input
+ * and output.
+ *   - TSA_ERR_UNSUPPORTED when the problem's scratch
+ *     (tsa_fused_workspace_bytes) exceeds TSA_NOALLOC_SCRATCH_BYTES;
+ *     about 49 MiB at B=1, Hq=32, L=128K, w=64.
+ *   - The scratch is resolved on the stream's device (the current device for
+ *     the null stream) on its first call there; make that first call outside
+ *     graph capture.
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents (the kernels clear what must start at zero).  Calls
+ *     that overlap on one GPU (different streams or threads, no ordering
+ *     between them) race on it and give undefined results. */
+tsa_status tsa_forward_fused_noalloc(const tsa_problem* prob, const void* q, const void* k,
+                                     const void* v, void* o, int32_t* budget, int32_t* idx,
+                                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,8 @@ EXPORTS = ["tsa_status_string", "tsa_last_error", "tsa_version", "tsa_workspace_
            "tsa_forward_workspace_bytes", "tsa_score", "tsa_budget", "tsa_select", "tsa_gather",
            "tsa_attention", "tsa_scatter", "tsa_forward", "tsa_fused_workspace_bytes",
            "tsa_attention_indexed", "tsa_forward_fused", "tsa_zero_unselected",
-           "tsa_block_mask_words", "tsa_attention_block_sparse", "tsa_attention_qo_indexed"]
+           "tsa_block_mask_words", "tsa_attention_block_sparse", "tsa_attention_qo_indexed",
+           "tsa_forward_fused_noalloc"]
 
 
 class TsaProblem(ctypes.Structure):
@@ -54,7 +55,10 @@ _SIGNATURES = {
     "tsa_zero_unselected": (ctypes.c_int, [_P, _vp, _vp, _vp]),
     "tsa_block_mask_words": (_sz, [_P]),
     "tsa_attention_block_sparse": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "tsa_forward_fused_noalloc": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
+
+NOALLOC_SCRATCH_BYTES = 128 << 20    # TSA_NOALLOC_SCRATCH_BYTES in include/tsa.h
 
 _lib = None
 

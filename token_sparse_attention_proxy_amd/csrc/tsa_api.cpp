@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "tsa_internal.h"
@@ -91,6 +92,51 @@ tsa_status launched(hipError_t err, const char* what) {
 
 tsa_status injected(const char* what) {
   return fail(TSA_ERR_HIP, "%s: injected launch failure (TSA_FAULT_INJECT)", what);
+}
+
+// ---------------------------------------------------------------- no-allocation scratch
+// Library-owned scratch of tsa_forward_fused_noalloc: one copy of this array
+// lives on every GPU the library runs on, for the life of the process.  Host
+// code never uses the array's name as an address (on the host it is only a
+// stand-in for the symbol); each device's address comes from
+// hipGetSymbolAddress, taken once with that device current.
+constexpr size_t kNoAllocBytes = size_t(TSA_NOALLOC_SCRATCH_BYTES);
+static_assert(kNoAllocBytes % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};   // per device, filled on first use
+
+// Device address of this device's scratch array (resolved once per device).
+tsa_status scratch_for(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(TSA_ERR_UNSUPPORTED, "device %d is beyond the %d the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    hipError_t err = hipGetDevice(&cur);
+    if (err == hipSuccess && cur != dev) err = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (err == hipSuccess) err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (err == hipSuccess) err = back;
+    }
+    if (err != hipSuccess || !ptr)
+      return fail(TSA_ERR_HIP, "scratch address on device %d: %s", dev, hipGetErrorString(err));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TSA_OK;
+}
+
+// The device a stream belongs to (the current device for the null stream).
+tsa_status stream_device(hipStream_t st, int* dev) {
+  hipError_t err = st ? hipStreamGetDevice(st, dev) : hipGetDevice(dev);
+  if (err != hipSuccess) return fail(TSA_ERR_HIP, "stream device: %s", hipGetErrorString(err));
+  return TSA_OK;
 }
 
 #define TSA_TRY(expr)                 \
@@ -370,36 +416,78 @@ tsa_status tsa_zero_unselected(const tsa_problem* prob, const int32_t* rank, voi
                   "tsa_zero_unselected");
 }
 
-tsa_status tsa_forward_fused(const tsa_problem* prob, const void* q, const void* k, const void* v,
-                             void* o, int32_t* budget, int32_t* idx, void* ws, size_t ws_bytes,
-                             void* stream) {
-  tsa::Shape sh;
-  TSA_TRY(check_problem(prob, &sh));
+}  // extern "C"
+
+namespace {
+
+// The kernels of the fused whole op, with their scratch at `base` (the
+// layout of tsa::fwd_ws_layout up to fused_total).
+tsa_status run_forward_fused(const tsa::Shape& sh, const void* q, const void* k, const void* v,
+                             void* o, int32_t* budget, int32_t* idx, char* base, hipStream_t st,
+                             const char* what) {
+  const tsa::FwdWs f = tsa::fwd_ws_layout(sh);
+  float* scores = reinterpret_cast<float*>(base + f.scores);
+  int32_t* rank = reinterpret_cast<int32_t*>(base + f.rank);
+  hipError_t err;
+  if ((err = tsa::launch_score(sh, q, k, scores, base, st)) != hipSuccess)
+    return launched(err, what);
+  if ((err = tsa::launch_budget(sh, scores, budget, base, st)) != hipSuccess)
+    return launched(err, what);
+  if ((err = tsa::launch_select(sh, scores, budget, idx, rank, base, st)) != hipSuccess)
+    return launched(err, what);
+  if ((err = tsa::launch_zero_unselected(sh, rank, o, st)) != hipSuccess)
+    return launched(err, what);
+  if ((err = tsa::launch_attention(sh, q, k, v, budget, idx, sh.Hq / sh.Hkv, o, st)) != hipSuccess)
+    return launched(err, what);
+  return ok();
+}
+
+tsa_status check_forward_args(const tsa_problem* prob, const void* q, const void* k,
+                              const void* v, const void* o, const int32_t* budget,
+                              const int32_t* idx, tsa::Shape* sh) {
+  TSA_TRY(check_problem(prob, sh));
   TSA_TRY(check_ptr(q, "q"));
   TSA_TRY(check_ptr(k, "k"));
   TSA_TRY(check_ptr(v, "v"));
   TSA_TRY(check_ptr(o, "o"));
   TSA_TRY(check_ptr(budget, "budget"));
   TSA_TRY(check_ptr(idx, "idx"));
-  const tsa::FwdWs f = tsa::fwd_ws_layout(sh);
-  TSA_TRY(check_ws(ws, ws_bytes, f.fused_total));
+  return TSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tsa_status tsa_forward_fused(const tsa_problem* prob, const void* q, const void* k, const void* v,
+                             void* o, int32_t* budget, int32_t* idx, void* ws, size_t ws_bytes,
+                             void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_forward_args(prob, q, k, v, o, budget, idx, &sh));
+  TSA_TRY(check_ws(ws, ws_bytes, tsa::fwd_ws_layout(sh).fused_total));
   if (fault_injected()) return injected("tsa_forward_fused");
-  char* base = static_cast<char*>(ws);
+  return run_forward_fused(sh, q, k, v, o, budget, idx, static_cast<char*>(ws),
+                           hipStream_t(stream), "tsa_forward_fused");
+}
+
+tsa_status tsa_forward_fused_noalloc(const tsa_problem* prob, const void* q, const void* k,
+                                     const void* v, void* o, int32_t* budget, int32_t* idx,
+                                     void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_forward_args(prob, q, k, v, o, budget, idx, &sh));
+  const size_t need = tsa::fwd_ws_layout(sh).fused_total;
+  if (need > kNoAllocBytes)
+    return fail(TSA_ERR_UNSUPPORTED,
+                "this problem needs %zu bytes of scratch; the no-allocation entry point holds "
+                "%zu (use tsa_forward_fused with a workspace)", need, kNoAllocBytes);
+  if (fault_injected()) return injected("tsa_forward_fused_noalloc");
   hipStream_t st = hipStream_t(stream);
-  float* scores = reinterpret_cast<float*>(base + f.scores);
-  int32_t* rank = reinterpret_cast<int32_t*>(base + f.rank);
-  hipError_t err;
-  if ((err = tsa::launch_score(sh, q, k, scores, base, st)) != hipSuccess)
-    return launched(err, "tsa_forward_fused/score");
-  if ((err = tsa::launch_budget(sh, scores, budget, base, st)) != hipSuccess)
-    return launched(err, "tsa_forward_fused/budget");
-  if ((err = tsa::launch_select(sh, scores, budget, idx, rank, base, st)) != hipSuccess)
-    return launched(err, "tsa_forward_fused/select");
-  if ((err = tsa::launch_zero_unselected(sh, rank, o, st)) != hipSuccess)
-    return launched(err, "tsa_forward_fused/zero");
-  if ((err = tsa::launch_attention(sh, q, k, v, budget, idx, sh.Hq / sh.Hkv, o, st)) != hipSuccess)
-    return launched(err, "tsa_forward_fused/attention");
-  return ok();
+  int dev = 0;
+  TSA_TRY(stream_device(st, &dev));
+  void* base = nullptr;
+  TSA_TRY(scratch_for(dev, &base));
+  return run_forward_fused(sh, q, k, v, o, budget, idx, static_cast<char*>(base), st,
+                           "tsa_forward_fused_noalloc");
 }
 
 }  // extern "C"
