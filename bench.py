@@ -24,7 +24,15 @@ Printed as one JSON line, with:
   * a synthetic 4-layer stack with random weights at the 32K shape (Hq=32,
     Hkv=8, d=128): every layer re-selects; per-layer K/L, overlap of the
     index sets of consecutive layers, and the stack's time against the same
-    stack with dense attention.
+    stack with dense attention;
+  * a sweep over the other workloads (8K; 32K with Zipf-biased keys at
+    tau = 0.01, 0.05, 0.1; B=2 64K with 7 query heads per KV head): ms per
+    layer of the op and of the dense attention, speedup, K/L, the share of
+    the non-attention kernels and the attention's MFMA fraction;
+  * per kernel, the HBM bytes that rocprofv3 counters recorded for the same
+    kernel source (profiles/traffic.json) beside its algorithmic bytes;
+  * provenance: source hashes, GPU, ROCm and torch versions, seeds, and a
+    parity check of a small case against the fp64 oracle.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--path fused|steps]
@@ -83,6 +91,141 @@ def block_sparse_flops(words: np.ndarray, n: int, d: int) -> float:
 def source_hash(path: str) -> str:
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+CSRC = os.path.join(ROOT, "token_sparse_attention_proxy_amd", "csrc")
+
+
+def load_traffic():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return {}
+
+
+def counter_bytes(tab: dict, kernels, workload: str):
+    """Sum of the counter bytes per launch of these kernels (short names), or None unless
+    every one was recorded for this workload from the kernel source as it is now."""
+    total = 0.0
+    for kn in kernels:
+        ent = tab.get(kn, {}).get(workload)
+        src = ent and os.path.join(CSRC, ent.get("source", "attention.hip"))
+        if not ent or not os.path.exists(src) or ent.get("source_sha") != source_hash(src):
+            return None
+        total += ent["bytes_per_launch"]
+    return total
+
+
+def provenance(wl, tau):
+    """Where and from what this line was measured."""
+    import subprocess
+    import torch
+    sha = None
+    try:
+        sha = subprocess.run(["git", "rev-parse", "--short=12", "HEAD"], cwd=ROOT, capture_output=True,
+                             text=True, timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp", ".h")))
+    h = hashlib.sha256()
+    for f in srcs:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    props = torch.cuda.get_device_properties(0)
+    return {"git_sha": sha, "csrc_sha": h.hexdigest()[:16], "bench_sha": source_hash(__file__),
+            "gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "rocm": torch.version.hip,
+            "torch": torch.__version__, "seed": wl.seed(0), "tau": tau}
+
+
+def parity_check():
+    """A small whole op against the fp64 oracle: budgets and index sets exact, outputs within
+    2e-2 of the largest reference output per head (the library's bf16 tolerance)."""
+    import torch
+    from oracle import tsa_oracle as O
+    from token_sparse_attention_proxy_amd import inputs
+    from token_sparse_attention_proxy_amd import tsa as T
+    wl = inputs.small_workload("bf16", B=1, Hq=8, Hkv=2, L=1500, d=128, w=64, tau=0.05,
+                               seed_base=9700)
+    q, k, v = inputs.make_qkv(wl)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v))
+    prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, 0.05, "bf16")
+    o, budget, idx = T.tsa_forward(prob, qd, kd, vd)
+    torch.cuda.synchronize()
+    ref = O.forward(q, k, v, wl.w, 0.05)
+    kb = int(budget.cpu()[0])
+    ok_budget = kb == int(ref["budget"][0])
+    idx_np = idx.cpu().numpy()
+    ok_sets = ok_budget and bool(np.array_equal(idx_np[0, :, :kb], ref["idx"][0, :, :kb]))
+    o_np = o.float().cpu().numpy().astype(np.float64)
+    worst = max(float(np.abs(o_np[0, h] - ref["o"][0, h]).max() / np.abs(ref["o"][0, h]).max())
+                for h in range(wl.Hq))
+    return {"case": wl.name, "budget_exact": ok_budget, "sets_exact": ok_sets,
+            "worst_rel_err": float(f"{worst:.3e}"), "ok": bool(ok_sets and worst <= 2e-2)}
+
+
+def sweep_one(name: str, taus, dev, steps: int):
+    """One workload of the sweep: the op (tsa_forward) per tau against the dense attention."""
+    import torch
+    from token_sparse_attention_proxy_amd import inputs
+    from token_sparse_attention_proxy_amd import tsa as T
+    wl = inputs.WORKLOADS[name]
+    q, k, v = inputs.make_qkv(wl)
+    qd, kd, vd = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v))
+    del q, k, v
+    st = torch.cuda.current_stream(dev)
+    shape = (wl.B, wl.Hq, wl.L, wl.d)
+    o = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    prob0 = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, float(taus[0]), "bf16")
+    dense_ms = timed(lambda: T.tsa_attention(prob0, qd, kd, vd, None, wl.G, o), max(2, steps // 2))
+    dense_tf = attention_flops([wl.L] * wl.B, wl.Hq, wl.d)
+    out = []
+    for tau in taus:
+        prob = dataclasses.replace(prob0, tau=float(tau))
+        ws = torch.empty(T.forward_workspace_bytes(prob), dtype=torch.uint8, device=dev)
+        budget = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+        idx = torch.empty((wl.B, wl.Hq, wl.L), dtype=torch.int32, device=dev)
+        ms = timed(lambda: T.tsa_forward(prob, qd, kd, vd, o, budget, idx, ws), steps)
+        bud = budget.cpu().numpy()
+        # the op's attention alone, on the compact K and V the op leaves in its workspace
+        s = torch.empty((wl.B, wl.Hq, wl.L), dtype=torch.float32, device=dev)
+        step_ws = torch.empty(T.workspace_bytes(prob), dtype=torch.uint8, device=dev)
+        T.tsa_score(prob, qd, kd, s, step_ws)
+        _, rank = T.tsa_select(prob, s, budget, None, None, step_ws)
+        kc, vc = T.tsa_gather_kv(prob, kd, vd, rank)
+        attn_ms = timed(lambda: T.tsa_attention_qo_indexed(prob, qd, kc, vc, idx, budget, o), steps)
+        fl = attention_flops(bud, wl.Hq, wl.d)
+        kl = bud / wl.L
+        rec = {"workload": name, "tau": float(tau), "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv,
+               "L": wl.L, "w": wl.w, "keep_frac": [round(float(x), 5) for x in kl],
+               "ms_per_layer": round(ms, 4), "dense_ms": round(dense_ms, 4),
+               "speedup_vs_dense": round(dense_ms / ms, 4),
+               "attention_ms": round(attn_ms, 4),
+               "overhead_share": round((ms - attn_ms) / attn_ms, 4),
+               "attention_mfma_frac": round(fl / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "dense_mfma_frac": round(dense_tf / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench] sweep {name} tau={tau}: {ms:.3f} ms vs dense {dense_ms:.3f} ms "
+            f"(x{dense_ms / ms:.3f}), K/L {kl.round(4)}, attention {attn_ms:.3f} ms, "
+            f"overhead {rec['overhead_share']:.4f}")
+        out.append(rec)
+        del ws, budget, idx, s, step_ws, rank, kc, vc
+    del qd, kd, vd, o
+    torch.cuda.empty_cache()
+    return out
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -169,6 +312,7 @@ def main():
     ap.add_argument("--no-readings", action="store_true")
     ap.add_argument("--no-block-sparse", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -239,7 +383,7 @@ def main():
         "budget": lambda: T.tsa_budget(prob, s, budget, step_ws),
         "select": lambda: T.tsa_select(prob, s, budget, idx, rank, step_ws),
         "gather": lambda: T.tsa_gather(prob, qd, kd, vd, idx, budget, qc, kc, vc),
-        "gather_kv": lambda: T.tsa_gather(prob, qd, kd, vd, idx, budget, None, kc, vc, with_q=False),
+        "gather_kv": lambda: T.tsa_gather_kv(prob, kd, vd, rank, kc, vc),
         "attention": lambda: T.tsa_attention(prob, qc, kc, vc, budget, 1, oc),
         "scatter": lambda: T.tsa_scatter(prob, oc, rank, o),
         "zero_fill": lambda: T.tsa_zero_unselected(prob, rank, o),
@@ -413,7 +557,7 @@ def main():
         "budget": 4 * heads * wl.L,
         "select": 4 * heads * wl.L + 4 * Ksum + 4 * heads * wl.L,
         "gather": Ksum * row + 2 * uniq * row + 3 * Ksum * row + 4 * Ksum,
-        "gather_kv": 2 * uniq * row + 2 * Ksum * row + 4 * Ksum,
+        "gather_kv": 2 * uniq * row + 2 * Ksum * row + 4 * heads * wl.L,
         "scatter": Ksum * row + heads * wl.L * row + 4 * heads * wl.L,
         "zero_fill": 4 * heads * wl.L + (heads * wl.L - Ksum) * row,
     }
@@ -422,6 +566,25 @@ def main():
                    "GB_s": round(hbm_bytes[n] / (steps_ms[n] * 1e-3) / 1e9, 1),
                    "hbm_frac": round(hbm_bytes[n] / (steps_ms[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                    "algorithmic_bytes": int(hbm_bytes[n])} for n in hbm_bytes}
+    # HBM bytes from rocprofv3 FETCH_SIZE + WRITE_SIZE of the same kernel sources (null when a
+    # source changed since they were recorded), and their ratio to the algorithmic bytes
+    vpr = wl.d * eb // 16
+    step_kernels = {
+        "score": [f"score_mfma_rowstats<{wl.d}>", "score_merge", f"score_mfma_colsum<{wl.d}>"],
+        "budget": ["clear_words", "budget_sigma", "budget_extract", "budget_cut"],
+        "select": ["sel_clear", "sel_level<0>", "sel_level<1>", "sel_level<2>", "sel_count",
+                   "sel_compact"],
+        "gather": [f"gather_rows<{vpr}, true, 32>"],
+        "gather_kv": [f"gather_kv_by_rank<{vpr}>"],
+        "scatter": [f"scatter_rows<{vpr}>"],
+        "zero_fill": [f"zero_rows<{vpr}>"],
+    }
+    traffic_tab = load_traffic()
+    for n, kns in step_kernels.items():
+        cb = counter_bytes(traffic_tab, kns, wl.name) if bf16 else None
+        kernels[n]["counter_bytes"] = None if cb is None else int(cb)
+        kernels[n]["counter_over_algorithmic"] = None if cb is None else round(cb / hbm_bytes[n], 3)
+        kernels[n]["counter_GB_s"] = None if cb is None else round(cb / (steps_ms[n] * 1e-3) / 1e9, 1)
     # proxy scoring also runs MFMA work and exps: two passes, each over every (proxy row, key)
     sc_s = steps_ms["score"] * 1e-3
     sc_rows = heads * 32 * ((wl.w + 31) // 32)          # proxy rows padded to whole 32-row tiles
@@ -469,8 +632,20 @@ def main():
         "readings": readings,
         "block_sparse": block_sparse,
         "stack": stack_rep,
+        "sweep": None,
+        "provenance": provenance(wl, tau),
+        "parity": None,
         "cpu_baseline": None,
     }
+    log("[bench] parity check against the oracle")
+    out["parity"] = parity_check()
+    if not args.no_sweep:
+        sweep = []
+        for name, taus in [("llama8b_bf16_L8k", (0.05,)), ("llama8b_bf16_L32k_zipf", (0.01, 0.05, 0.1)),
+                           ("gqa7_bf16_B2_L64k", (0.1,))]:
+            log(f"[bench] sweep {name}: generating inputs")
+            sweep += sweep_one(name, taus, dev, max(3, min(args.steps, 10)))
+        out["sweep"] = sweep
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")
         out["cpu_baseline"] = cpu_baseline(wl, q, k, v, tau, int(bud[0]))

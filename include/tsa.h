@@ -155,6 +155,17 @@ tsa_status tsa_gather(const tsa_problem* prob, const void* q, const void* k, con
                       const int32_t* idx, const int32_t* budget, void* qc, void* kc, void* vc,
                       void* stream);
 
+/* Compression of K and V only ("Core architecture", stage 1), source-driven:
+ * every K/V row of a KV head is read once and written to each of its query
+ * heads that selected it,
+ *   kc[b,h,rank[b,h,j]] = K[b,g(h),j], vc[b,h,rank[b,h,j]] = V[b,g(h),j]
+ * for every j with rank[b,h,j] >= 0.  With rank as tsa_select writes it, this
+ * is tsa_gather with qc = NULL, bit for bit; tsa_forward runs it.  k, v:
+ * [B,Hkv,L,d]; rank: [B,Hq,L] int32 (values in [-1, L)); kc, vc: [B,Hq,L,d]
+ * outputs (rows at or past K_b are not written). */
+tsa_status tsa_gather_kv(const tsa_problem* prob, const void* k, const void* v,
+                         const int32_t* rank, void* kc, void* vc, void* stream);
+
 /* Causal attention on dense tensors (the compressed tensors, or the
  * uncompressed ones for the dense baseline).  For i < n:
  *   o[b,h,i] = sum_{j<=i} softmax_j(<q[b,h,i], k[b,h/kv_group,j]>/sqrt(d)) v[b,h/kv_group,j]

@@ -127,6 +127,7 @@ def _call_all(lib, p, ptr=FAKE, ws_bytes=1 << 40, kv_group=1):
         "budget": lib.tsa_budget(P, ptr, ptr, ptr, ws_bytes, None),
         "select": lib.tsa_select(P, ptr, ptr, ptr, ptr, ptr, ws_bytes, None),
         "gather": lib.tsa_gather(P, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, None),
+        "gather_kv": lib.tsa_gather_kv(P, ptr, ptr, ptr, ptr, ptr, None),
         "attention": lib.tsa_attention(P, ptr, ptr, ptr, ptr, kv_group, ptr, None),
         "scatter": lib.tsa_scatter(P, ptr, ptr, ptr, None),
         "forward": lib.tsa_forward(P, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ws_bytes, None),

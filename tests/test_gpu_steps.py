@@ -89,6 +89,31 @@ def test_budget_matches_oracle(case):
         assert np.array_equal(got, want), (tau, got, want)
 
 
+@pytest.mark.parametrize("B,Hq,L", [(2, 3, 20000), (1, 32, 131072)])
+def test_budget_all_equal(B, Hq, L):
+    """Every token with the same importance: the whole sequence falls into one bucket of the
+    first pass, more values than the cut holds in LDS, so it runs from global memory."""
+    say(f"case budget all equal B={B} Hq={Hq} L={L}")
+    s = np.full((B, Hq, L), 1.0 / L, np.float32)
+    sd = to_dev(s, "f32")
+    for tau in (1e-4, 0.05, 0.3, 0.9):
+        got = to_np(T.tsa_budget(T.Problem(B, Hq, Hq, L, 128, 1, tau, "bf16"), sd))
+        want = O.coverage_budget(s.astype(np.float64), tau)
+        assert np.array_equal(got, want), (tau, got, want)
+
+
+def test_budget_long_sequence():
+    """Many workgroups per row in the first two passes (one chunk of the sequence each)."""
+    B, Hq, L = 2, 5, 150001
+    say(f"case budget long B={B} Hq={Hq} L={L}")
+    s = inputs.make_scores(B, Hq, L, seed=21, ties=False, zero_frac=0.05, alpha=1.0)
+    sd = to_dev(s, "f32")
+    for tau in (0.01, 0.05, 0.2):
+        got = to_np(T.tsa_budget(T.Problem(B, Hq, Hq, L, 128, 1, tau, "bf16"), sd))
+        want = O.coverage_budget(s.astype(np.float64), tau)
+        assert np.array_equal(got, want), (tau, got, want)
+
+
 def test_budget_exact_boundary():
     """tau equal to a pruned-mass value: the token at the boundary is pruned (<=)."""
     say("case budget boundary")
@@ -108,6 +133,9 @@ SELECT_CASES = [
     (1, 3, 1, 13, False),
     (1, 5, 3000, 14, True),
     (2, 6, 1025, 15, False),
+    # 20 chunks per head; dyadic ties spread over the chunk boundaries
+    (1, 2, 20000, 16, True),
+    (1, 1, 70001, 17, False),
 ]
 
 
@@ -187,6 +215,32 @@ def test_gather_scatter_bit_exact(case):
     bits = o.view(torch.int16 if dt == "bf16" else torch.int32)
     unsel = torch.from_numpy(rank < 0).cuda()
     assert torch.all(bits[unsel] == 0), "unselected rows must be +0.0 bit patterns"
+
+
+@pytest.mark.parametrize("case", GATHER_CASES + [("bf16", 2, 14, 2, 3000, 128, 2500)],
+                         ids=[str(c) for c in GATHER_CASES + [("bf16", 2, 14, 2, 3000, 128, 2500)]])
+def test_gather_kv_by_rank_bit_exact(case):
+    """The source-driven K/V gather (through the rank map) writes the oracle's compact K and V
+    and leaves the rows past the budget untouched."""
+    dt, B, Hq, Hkv, L, d, K = case
+    say(f"case gather_kv by rank {case}")
+    k = inputs.make_dense((B, Hkv, L, d), 26, dt)
+    v = inputs.make_dense((B, Hkv, L, d), 27, dt)
+    budget = np.array([K] + [max(1, K // 2)] * (B - 1), np.int32)
+    idx, rank = inputs.make_indices(B, Hq, L, budget, seed=28)
+    prob = T.Problem(B, Hq, Hkv, L, d, 1, 0.05, dt)
+    fill = torch.full((B, Hq, L, d), 7.0, dtype=torch.bfloat16 if dt == "bf16" else torch.float32,
+                      device="cuda")
+    kc, vc = T.tsa_gather_kv(prob, to_dev(k, dt), to_dev(v, dt), torch.from_numpy(rank).cuda(),
+                             fill.clone(), fill.clone())
+    q0 = np.zeros((B, Hq, L, d), np.float32)
+    _, rk, rv = O.gather(q0, k, v, idx, budget)
+    for b in range(B):
+        n = int(budget[b])
+        for got, want in ((kc, rk), (vc, rv)):
+            g = to_np(got)[b]
+            assert np.array_equal(g[:, :n], want[b, :, :n])
+            assert np.all(g[:, n:] == 7.0)
 
 
 ATTN_CASES = [

@@ -21,7 +21,7 @@ EXPORTS = ["tsa_status_string", "tsa_last_error", "tsa_version", "tsa_workspace_
            "tsa_attention", "tsa_scatter", "tsa_forward", "tsa_fused_workspace_bytes",
            "tsa_attention_indexed", "tsa_forward_fused", "tsa_zero_unselected",
            "tsa_block_mask_words", "tsa_attention_block_sparse", "tsa_attention_qo_indexed",
-           "tsa_forward_fused_noalloc"]
+           "tsa_forward_fused_noalloc", "tsa_gather_kv"]
 
 
 class TsaProblem(ctypes.Structure):
@@ -56,6 +56,7 @@ _SIGNATURES = {
     "tsa_block_mask_words": (_sz, [_P]),
     "tsa_attention_block_sparse": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "tsa_forward_fused_noalloc": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "tsa_gather_kv": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 NOALLOC_SCRATCH_BYTES = 128 << 20    # TSA_NOALLOC_SCRATCH_BYTES in include/tsa.h

@@ -10,11 +10,22 @@
 // With C(p) the sum of the p smallest sigma and thr = floor(Hq*tau*2^50):
 //   P = max{p in [0, L-1] : C(p) <= thr},  budget = L - P   (tau = 0: L).
 //
-// The cut is found without sorting: a most-significant-digit radix descent
-// over the sigma values keeps (count, mass) histograms and at each level
-// moves into the first digit bucket where the running mass exceeds thr.  It
-// stops when that bucket holds one value or all bits are fixed; all values
-// left in the bucket are then equal, and P follows in closed form.
+// The cut is found without sorting, over the whole GPU:
+//   1. sigma pass (many workgroups): sigma_j, and a histogram of (count,
+//      exact mass) over 4096 log-scale buckets of sigma (bit length and the
+//      six bits after the leading one: monotonic in sigma), merged into a
+//      global histogram with integer atomics;
+//   2. extract pass (many workgroups): every workgroup scans the histogram
+//      in ascending order to the first bucket where the running mass
+//      exceeds thr (the same integer scan everywhere), and copies that
+//      bucket's values into a candidate list (order free: only the multiset
+//      matters below);
+//   3. cut (one workgroup per budget row): every value below the bucket is
+//      pruned; inside it, a most-significant-digit radix descent over the
+//      candidates (in LDS when they fit) moves into the first digit bucket
+//      whose running mass exceeds what is left of thr, and stops when that
+//      bucket holds one value or all bits are fixed; all values left are
+//      then equal and P follows in closed form.
 //
 // Alternative readings: with per-head budgets each (b, h) is a row of its
 // own (sigma = that head's quantised scores, thr = floor(tau*2^50)); with a
@@ -26,28 +37,17 @@
 namespace tsa {
 namespace {
 
-constexpr int kSigmaThreads = 256;
+constexpr int kThreads = 256;                // sigma and extract passes
+constexpr int kPer = 4;                      // sigma pass: tokens per thread (one 16-byte load per head)
+constexpr int kSigChunk = kThreads * kPer;   // tokens per sigma workgroup
+constexpr int kExPer = 8;                    // extract pass: tokens per thread
+constexpr int kExChunk = kThreads * kExPer;  // tokens per extract workgroup
+constexpr int kLogBuckets = kBudgetLogBuckets;   // 4096: 6 bits of bit length, 6 after the leading one
+constexpr int kLogPerThread = kLogBuckets / kThreads;
 constexpr int kCutThreads = 1024;
 constexpr int kDigitBits = 11;
 constexpr int kBuckets = 1 << kDigitBits;
-constexpr int kPer = 4;                      // sigma values per thread per step of the cut
-constexpr int kStep = kCutThreads * kPer;
-
-// sigma[j0 .. j0 + kPer) (0 past nc); two 16-byte loads when aligned.
-__device__ __forceinline__ void load_vals(const uint64_t* __restrict__ sg, int j0, int nc, bool vec,
-                                          uint64_t (&v)[kPer]) {
-  if (vec && j0 + kPer <= nc) {
-#pragma unroll
-    for (int q = 0; q < kPer; q += 2) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(sg + j0 + q);
-      v[q] = uint64_t(x[0]) | (uint64_t(x[1]) << 32);
-      v[q + 1] = uint64_t(x[2]) | (uint64_t(x[3]) << 32);
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) v[q] = j0 + q < nc ? sg[j0 + q] : 0;
-  }
-}
+constexpr int kCandLds = 12288;              // candidates held in LDS by the cut (96 KiB)
 
 __device__ __forceinline__ uint64_t quantise(float x) {
   // fmaxf/fminf return the non-NaN operand, so NaN counts as 0.
@@ -55,48 +55,184 @@ __device__ __forceinline__ uint64_t quantise(float x) {
   return uint64_t(double(x) * 1125899906842624.0);   // * 2^50, exact; truncation = floor
 }
 
-__global__ void clear_u64(uint64_t* __restrict__ p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
+// Log-scale bucket of v: (bit length) * 64 + the six bits after the leading
+// one (the low bits, zero-padded, when v has fewer than seven bits).  Equal
+// values share a bucket and a larger value never gets a smaller bucket.
+__device__ __forceinline__ int log_bucket(uint64_t v) {
+  if (v == 0) return 0;
+  const int e = 64 - __clzll((long long)v);           // 1 .. 64
+  const uint32_t m = e >= 7 ? uint32_t(v >> (e - 7)) & 63u : uint32_t(v << (7 - e)) & 63u;
+  return (min(e, 63) << 6) | int(m);
 }
 
-// sigma[r,j] = sum over the hpr query heads of budget row r, in head order,
-// of the quantised score, for the nc candidate tokens j < nc.
-__global__ __launch_bounds__(kSigmaThreads) void budget_sigma(const float* __restrict__ s,
-                                                              uint64_t* __restrict__ sigma,
-                                                              uint64_t* __restrict__ sigmax,
-                                                              int hpr, int L, int nc) {
-  __shared__ uint64_t red[kSigmaThreads / 64];
-  const int b = blockIdx.y;
-  const int j = blockIdx.x * kSigmaThreads + threadIdx.x;
-  uint64_t acc = 0;
-  if (j < nc) {
-    const float* sb = s + int64_t(b) * hpr * L + j;
-    for (int h = 0; h < hpr; ++h) acc += quantise(sb[int64_t(h) * L]);
-    sigma[int64_t(b) * L + j] = acc;
+__global__ void clear_words(uint32_t* __restrict__ p, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// sigma[r,j] = sum over the hpr query heads of budget row r of the quantised
+// score (exact integers, so the order does not matter), for the nc candidate
+// tokens j < nc; and the row's log-bucket histogram of sigma (count, mass),
+// gathered in LDS per workgroup and merged into the row's histogram with
+// integer atomics.
+__global__ __launch_bounds__(kThreads) void budget_sigma(const float* __restrict__ s,
+                                                         uint64_t* __restrict__ sigma,
+                                                         uint32_t* __restrict__ hcnt,
+                                                         uint64_t* __restrict__ hmass, int hpr,
+                                                         int L, int nc) {
+  __shared__ uint32_t lc[kLogBuckets];
+  __shared__ uint64_t lm[kLogBuckets];
+  const int r = blockIdx.y;
+  const int t = threadIdx.x;
+  for (int i = t; i < kLogBuckets; i += kThreads) {
+    lc[i] = 0u;
+    lm[i] = 0u;
   }
-  // block max, then one integer atomic per block
-  uint64_t m = acc;
+  const int j = int(blockIdx.x) * kSigChunk + kPer * t;
+  const float* sr = s + int64_t(r) * hpr * L;
+  const bool vec = (L % kPer) == 0 && (reinterpret_cast<uintptr_t>(s) % 16) == 0;
+  uint64_t acc[kPer] = {0, 0, 0, 0};
+  if (vec && j + kPer <= nc) {
+#pragma unroll 8
+    for (int h = 0; h < hpr; ++h) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(sr + int64_t(h) * L + j);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint64_t y = __shfl_xor(m, o, 64);
-    m = y > m ? y : m;
+      for (int q = 0; q < kPer; ++q) acc[q] += quantise(x[q]);
+    }
+  } else {
+    for (int h = 0; h < hpr; ++h)
+#pragma unroll
+      for (int q = 0; q < kPer; ++q)
+        if (j + q < nc) acc[q] += quantise(sr[int64_t(h) * L + j + q]);
   }
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();                        // the LDS histogram is clear
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    if (j + q < nc) {
+      sigma[int64_t(r) * L + j + q] = acc[q];
+      const int bk = log_bucket(acc[q]);
+      atomicAdd(&lc[bk], 1u);
+      atomicAdd(reinterpret_cast<unsigned long long*>(&lm[bk]), (unsigned long long)acc[q]);
+    }
+  }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t mm = 0;
-    for (int i = 0; i < kSigmaThreads / 64; ++i) mm = red[i] > mm ? red[i] : mm;
-    atomicMax(reinterpret_cast<unsigned long long*>(sigmax + b), (unsigned long long)mm);
+  uint32_t* gc = hcnt + int64_t(r) * kLogBuckets;
+  uint64_t* gm = hmass + int64_t(r) * kLogBuckets;
+  for (int i = t; i < kLogBuckets; i += kThreads) {
+    if (lc[i]) {
+      atomicAdd(&gc[i], lc[i]);
+      atomicAdd(reinterpret_cast<unsigned long long*>(&gm[i]), (unsigned long long)lm[i]);
+    }
   }
 }
 
-// One workgroup per budget row: radix descent for the coverage cut over the
-// nc candidates; P is at most pmax.
-__global__ __launch_bounds__(kCutThreads) void budget_cut(const uint64_t* __restrict__ sigma,
-                                                          const uint64_t* __restrict__ sigmax,
+// Ascending scan of the log histogram: the first bucket whose running mass
+// exceeds thr, with the count and mass of all buckets below it
+// (crossed = 0: the whole candidate mass stays within thr).  The same in
+// every workgroup; contains barriers.
+struct Cross {
+  uint64_t mass_below, cnt_below;
+  int bucket, crossed;
+};
+__device__ __forceinline__ Cross find_cross(const uint32_t* __restrict__ hc,
+                                            const uint64_t* __restrict__ hm, uint64_t thr,
+                                            uint64_t* tmp, uint64_t* sh) {
+  const int t = threadIdx.x;
+  const int d0 = kLogPerThread * t;              // this thread's buckets, ascending
+  uint64_t m[kLogPerThread];
+  uint64_t msum = 0, csum = 0;
+#pragma unroll
+  for (int i = 0; i < kLogPerThread; ++i) {
+    m[i] = hm[d0 + i];
+    msum += m[i];
+    csum += hc[d0 + i];
+  }
+  if (t == 0) sh[0] = kLogBuckets;
+  uint64_t tot;
+  const uint64_t mex = block_excl_scan_u64(msum, tmp, &tot);
+  const uint64_t cex = block_excl_scan_u64(csum, tmp, &tot);
+  uint64_t run = mex;
+  int found = -1;
+#pragma unroll
+  for (int i = 0; i < kLogPerThread; ++i) {
+    if (found < 0 && run + m[i] > thr) found = d0 + i;
+    run += m[i];
+  }
+  if (found >= 0) atomicMin(reinterpret_cast<unsigned long long*>(&sh[0]), (unsigned long long)found);
+  __syncthreads();
+  Cross c;
+  c.bucket = int(sh[0]);
+  c.crossed = c.bucket < kLogBuckets;
+  if (c.crossed && t == c.bucket / kLogPerThread) {
+    uint64_t mb = mex, cb = cex;
+#pragma unroll
+    for (int i = 0; i < kLogPerThread; ++i)
+      if (d0 + i < c.bucket) {
+        mb += m[i];
+        cb += hc[d0 + i];
+      }
+    sh[1] = mb;
+    sh[2] = cb;
+  }
+  __syncthreads();
+  c.mass_below = c.crossed ? sh[1] : 0;
+  c.cnt_below = c.crossed ? sh[2] : 0;
+  __syncthreads();
+  return c;
+}
+
+// The values of the crossing bucket, appended to cand[r] (ncand[r] counts
+// them; one atomic per workgroup reserves its slots).  Workgroup (0, r) also
+// records the crossing: state[r] = (bucket, mass below, count below, crossed).
+__global__ __launch_bounds__(kThreads) void budget_extract(
+    const uint64_t* __restrict__ sigma, const uint32_t* __restrict__ hcnt,
+    const uint64_t* __restrict__ hmass, uint64_t* __restrict__ cand, uint32_t* __restrict__ ncand,
+    uint64_t* __restrict__ state, int L, int nc, uint64_t thr) {
+  __shared__ uint64_t tmp[17];
+  __shared__ uint64_t sh[3];
+  __shared__ uint32_t base_s;
+  const int r = blockIdx.y;
+  const int t = threadIdx.x;
+  const Cross c = find_cross(hcnt + int64_t(r) * kLogBuckets, hmass + int64_t(r) * kLogBuckets, thr,
+                             tmp, sh);
+  if (blockIdx.x == 0 && t == 0) {
+    state[int64_t(r) * 4 + 0] = uint64_t(c.bucket);
+    state[int64_t(r) * 4 + 1] = c.mass_below;
+    state[int64_t(r) * 4 + 2] = c.cnt_below;
+    state[int64_t(r) * 4 + 3] = uint64_t(c.crossed);
+  }
+  if (!c.crossed) return;                          // whole workgroup
+  const int j0 = int(blockIdx.x) * kExChunk + kExPer * t;
+  const uint64_t* sg = sigma + int64_t(r) * L;
+  uint64_t v[kExPer];
+  uint32_t nhit = 0;
+#pragma unroll
+  for (int q = 0; q < kExPer; ++q) {
+    const int j = j0 + q;
+    v[q] = j < nc ? sg[j] : 0;
+    const bool hit = j < nc && log_bucket(v[q]) == c.bucket;
+    nhit += hit;
+    if (!hit) v[q] = ~uint64_t(0);               // marks a miss (no sigma reaches 2^64 - 1)
+  }
+  uint64_t total;
+  const uint64_t off = block_excl_scan_u64(nhit, tmp, &total);
+  if (total == 0) return;                          // whole workgroup
+  if (t == 0) base_s = atomicAdd(&ncand[r], uint32_t(total));
+  __syncthreads();
+  uint64_t* cr = cand + int64_t(r) * L + base_s + off;
+  uint32_t k = 0;
+#pragma unroll
+  for (int q = 0; q < kExPer; ++q)
+    if (v[q] != ~uint64_t(0)) cr[k++] = v[q];
+}
+
+// One workgroup per budget row: the exact cut inside the crossing bucket.
+__global__ __launch_bounds__(kCutThreads) void budget_cut(const uint64_t* __restrict__ cand_g,
+                                                          const uint32_t* __restrict__ ncand,
+                                                          const uint64_t* __restrict__ state,
                                                           int32_t* __restrict__ budget, int L,
-                                                          int nc, int pmax, uint64_t thr) {
+                                                          int pmax, uint64_t thr) {
+  __shared__ uint64_t cand_s[kCandLds];
   __shared__ uint32_t cnt[kBuckets];
   __shared__ uint64_t mass[kBuckets];
   __shared__ uint64_t scan_tmp[17];
@@ -104,19 +240,31 @@ __global__ __launch_bounds__(kCutThreads) void budget_cut(const uint64_t* __rest
   __shared__ uint64_t sh_below_mass, sh_bucket_mass;
   __shared__ uint32_t sh_below_cnt, sh_bucket_cnt;
 
-  const int b = blockIdx.x;
+  const int r = blockIdx.x;
   const int t = threadIdx.x;
-  const uint64_t* sg = sigma + int64_t(b) * L;
-  const bool vec = (L % 2) == 0 && (reinterpret_cast<uintptr_t>(sigma) % 16) == 0;   // 16-byte rows
-  const uint64_t maxv = sigmax[b];
-  int lo = maxv ? 64 - __clzll((long long)maxv) : 1;   // bits above `lo` are zero for all values
-  uint64_t prefix = 0;          // value of bits [lo + width, 64) shared by the candidates
-  uint64_t mass_below = 0;      // exact mass of all values below the candidate range
-  uint64_t cnt_below = 0;
-  uint64_t n_eq = 0, T = 0;
-  bool crossed = true;
-
-  while (true) {
+  const int bucket = int(state[int64_t(r) * 4 + 0]);
+  const uint64_t mass_out = state[int64_t(r) * 4 + 1];   // pruned: every value below the bucket
+  const uint64_t cnt_out = state[int64_t(r) * 4 + 2];
+  const bool crossed = state[int64_t(r) * 4 + 3] != 0;
+  if (!crossed) {                       // the whole candidate mass stays within thr
+    if (t == 0) budget[r] = L - pmax;
+    return;
+  }
+  const int n = int(ncand[r]);
+  const uint64_t* cand = cand_g + int64_t(r) * L;
+  if (n <= kCandLds) {
+    for (int i = t; i < n; i += kCutThreads) cand_s[i] = cand[i];
+    cand = cand_s;                      // generic pointer to LDS from here on
+  }
+  __syncthreads();
+  // Every candidate shares the bit length e and the top seven bits.
+  const int e = bucket >> 6;
+  int lo = e > 7 ? e - 7 : 0;           // bits below the shared prefix
+  const uint64_t room = thr - mass_out;
+  uint64_t prefix = n > 0 ? (cand[0] >> lo) : 0;
+  uint64_t mass_below = 0, cnt_below = 0;   // within the bucket
+  uint64_t n_eq = uint64_t(n), T = n > 0 ? cand[0] : 1;
+  while (lo > 0) {
     const int width = lo < kDigitBits ? lo : kDigitBits;
     lo -= width;
     const int hi = lo + width;
@@ -126,22 +274,13 @@ __global__ __launch_bounds__(kCutThreads) void budget_cut(const uint64_t* __rest
     }
     if (t == 0) first_cross = kBuckets;
     __syncthreads();
-    // Four values per thread per step, the next step's loads issued first.
-    uint64_t v[kPer], vn[kPer];
-    load_vals(sg, kPer * t, nc, vec, v);
-    for (int base = 0; base < nc; base += kStep) {
-      load_vals(sg, base + kStep + kPer * t, nc, vec, vn);
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const uint64_t top = hi >= 64 ? 0 : (v[q] >> hi);
-        if (base + kPer * t + q < nc && top == prefix) {
-          const int dgt = int((v[q] >> lo) & uint64_t(kBuckets - 1));
-          atomicAdd(&cnt[dgt], 1u);
-          atomicAdd(reinterpret_cast<unsigned long long*>(&mass[dgt]), (unsigned long long)v[q]);
-        }
+    for (int i = t; i < n; i += kCutThreads) {
+      const uint64_t v = cand[i];
+      if ((v >> hi) == prefix) {
+        const int dgt = int((v >> lo) & uint64_t(kBuckets - 1));
+        atomicAdd(&cnt[dgt], 1u);
+        atomicAdd(reinterpret_cast<unsigned long long*>(&mass[dgt]), (unsigned long long)v);
       }
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) v[q] = vn[q];
     }
     __syncthreads();
     // Each thread owns two consecutive buckets; exclusive scan of their masses.
@@ -149,21 +288,15 @@ __global__ __launch_bounds__(kCutThreads) void budget_cut(const uint64_t* __rest
     const uint64_t m0 = mass[d0], m1 = mass[d0 + 1];
     uint64_t total;
     const uint64_t excl = block_excl_scan_u64(m0 + m1, scan_tmp, &total);
-    const uint64_t room = thr - mass_below;       // mass_below <= thr holds throughout
-    if (excl + m0 > room) atomicMin(&first_cross, d0);
-    else if (excl + m0 + m1 > room) atomicMin(&first_cross, d0 + 1);
+    const uint64_t left = room - mass_below;       // mass_below <= room holds throughout
+    if (excl + m0 > left) atomicMin(&first_cross, d0);
+    else if (excl + m0 + m1 > left) atomicMin(&first_cross, d0 + 1);
     __syncthreads();
-    const int dstar = first_cross;
-    if (dstar == kBuckets) {          // the whole candidate range stays within the threshold
-      crossed = false;
-      break;
-    }
-    // Mass of the buckets below d*: the owner of d* knows its prefix.
+    const int dstar = first_cross;    // exists: the bucket's total mass exceeds room
     if (t == (dstar >> 1)) {
       sh_below_mass = excl + ((dstar & 1) ? m0 : 0);
       sh_bucket_mass = (dstar & 1) ? m1 : m0;
     }
-    // Count below d*: a second scan over the counts.
     const uint64_t c01 = uint64_t(cnt[d0]) + cnt[d0 + 1];
     uint64_t ctot;
     const uint64_t cex = block_excl_scan_u64(c01, scan_tmp, &ctot);
@@ -179,20 +312,16 @@ __global__ __launch_bounds__(kCutThreads) void budget_cut(const uint64_t* __rest
     prefix = (prefix << width) | uint64_t(dstar);
     __syncthreads();
     if (n_eq == 1 || lo == 0) {
-      T = bucket_mass / n_eq;         // all values left in the bucket are equal
+      T = bucket_mass / n_eq;         // all values left in the digit bucket are equal
       break;
     }
   }
   if (t == 0) {
-    uint64_t P;
-    if (!crossed) {
-      P = uint64_t(pmax);
-    } else {
-      const uint64_t m = (thr - mass_below) / T;
-      P = cnt_below + (m < n_eq - 1 ? m : n_eq - 1);
-      if (P > uint64_t(pmax)) P = uint64_t(pmax);
-    }
-    budget[b] = int32_t(uint64_t(L) - P);
+    // T > 0: a crossing bucket has positive mass
+    const uint64_t m = (room - mass_below) / T;
+    uint64_t P = cnt_out + cnt_below + (m < n_eq - 1 ? m : n_eq - 1);
+    if (P > uint64_t(pmax)) P = uint64_t(pmax);
+    budget[r] = int32_t(uint64_t(L) - P);
   }
 }
 
@@ -212,7 +341,11 @@ hipError_t launch_budget(const Shape& sh, const float* scores, int32_t* budget, 
   }
   const StepWs lay = step_ws_layout(sh);
   uint64_t* sigma = reinterpret_cast<uint64_t*>(ws + lay.sigma);
-  uint64_t* sigmax = reinterpret_cast<uint64_t*>(ws + lay.sigmax);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(ws + lay.bud_cand);
+  uint32_t* hcnt = reinterpret_cast<uint32_t*>(ws + lay.bud_hcnt);
+  uint64_t* hmass = reinterpret_cast<uint64_t*>(ws + lay.bud_hmass);
+  uint32_t* ncand = reinterpret_cast<uint32_t*>(ws + lay.bud_ncand);
+  uint64_t* state = reinterpret_cast<uint64_t*>(ws + lay.bud_state);
   const int hpr = sh.per_head() ? 1 : sh.Hq;     // query heads per budget row
   const int nc = sh.L - sh.keep();                // pruning candidates
   const int pmax = nc < sh.L - 1 ? nc : sh.L - 1;
@@ -220,11 +353,14 @@ hipError_t launch_budget(const Shape& sh, const float* scores, int32_t* budget, 
   // the product is exact in double.
   const double x = double(hpr) * double(sh.tau) * 1125899906842624.0;
   const uint64_t thr = uint64_t(x);
-  clear_u64<<<(rows + 255) / 256, 256, 0, st>>>(sigmax, rows);
-  if (nc > 0)
-    budget_sigma<<<dim3((nc + kSigmaThreads - 1) / kSigmaThreads, rows), kSigmaThreads, 0, st>>>(
-        scores, sigma, sigmax, hpr, sh.L, nc);
-  budget_cut<<<rows, kCutThreads, 0, st>>>(sigma, sigmax, budget, sh.L, nc, pmax, thr);
+  // the count and mass histograms and the candidate counters are contiguous words
+  const int64_t words = (lay.bud_ncand + sizeof(uint32_t) * rows - lay.bud_hcnt) / sizeof(uint32_t);
+  clear_words<<<unsigned((words + 255) / 256), 256, 0, st>>>(hcnt, words);
+  budget_sigma<<<dim3((max(nc, 1) + kSigChunk - 1) / kSigChunk, rows), kThreads, 0, st>>>(
+      scores, sigma, hcnt, hmass, hpr, sh.L, nc);
+  budget_extract<<<dim3((max(nc, 1) + kExChunk - 1) / kExChunk, rows), kThreads, 0, st>>>(
+      sigma, hcnt, hmass, cand, ncand, state, sh.L, nc, thr);
+  budget_cut<<<rows, kCutThreads, 0, st>>>(cand, ncand, state, budget, sh.L, pmax, thr);
   return hipGetLastError();
 }
 

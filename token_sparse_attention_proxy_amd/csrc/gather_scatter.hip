@@ -12,6 +12,11 @@
 // zero_unselected: o[b,h,j] = 0 for every j with rank_j < 0.  It is the part
 // of decompression left when the attention kernel itself writes the
 // selected rows to their sequence positions.
+//
+// gather by rank (K and V only, the whole op): source-driven, each K/V row of
+// a KV head is read once and written to every query head of the group that
+// selected it, at its slot rank[b,h,j]: the same bytes as the gather, with
+// the shared source rows read once instead of once per query head.
 #include "tsa_device.h"
 #include "tsa_internal.h"
 
@@ -25,6 +30,7 @@ constexpr int kRowsGatherQKV = 32;
 constexpr int kRowsGatherKV = 128;
 constexpr int kRowsScatter = 32;
 constexpr int kRowsZero = 128;
+constexpr int kRowsByRank = 64;
 
 // VPR: 16-byte vectors per row (row bytes / 16).  One block copies compact
 // rows [i0, i0 + RPB) for all G query heads of one KV group, head
@@ -72,6 +78,49 @@ __global__ __launch_bounds__(kThreads) void gather_rows(
       if (i < i1) {
         const int64_t dst = (hrow + i) * VPR + vec;
         if constexpr (WQ) __builtin_nontemporal_store(aq[r], qc + dst);
+        __builtin_nontemporal_store(ak[r], kc + dst);
+        __builtin_nontemporal_store(av[r], vc + dst);
+      }
+    }
+  }
+}
+
+// One block takes source rows [j0, j0 + kRowsByRank) of one KV head (b, g):
+// every load (K, V and the G rank entries of each row) is issued before the
+// first store.
+template <int VPR>
+__global__ __launch_bounds__(kThreads) void gather_kv_by_rank(
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v, const int32_t* __restrict__ rank,
+    u32x4* __restrict__ kc, u32x4* __restrict__ vc, int Hq, int Hkv, int L, int nc) {
+  constexpr int kRowsPerPass = kThreads / VPR;
+  constexpr int R = kRowsByRank / kRowsPerPass;     // rows per thread
+  const int bg = blockIdx.y;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int G = Hq / Hkv;
+  const int j0 = blockIdx.x * kRowsByRank;
+  const int sub = threadIdx.x / VPR, vec = threadIdx.x % VPR;
+  const int64_t grow = (int64_t(b) * Hkv + g) * L;        // first row of (b,g)
+  const int64_t hrow0 = (int64_t(b) * Hq + int64_t(g) * G) * L;   // first row of head (b, gG)
+  u32x4 ak[R], av[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int j = j0 + sub + r * kRowsPerPass;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    ak[r] = j < nc ? k[(grow + j) * VPR + vec] : z;
+    av[r] = j < nc ? v[(grow + j) * VPR + vec] : z;
+  }
+  for (int hl = 0; hl < G; ++hl) {
+    const int64_t hrow = hrow0 + int64_t(hl) * L;
+    int slot[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int j = j0 + sub + r * kRowsPerPass;
+      slot[r] = j < nc ? rank[hrow + j] : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (slot[r] >= 0 && slot[r] < L) {
+        const int64_t dst = (hrow + slot[r]) * VPR + vec;
         __builtin_nontemporal_store(ak[r], kc + dst);
         __builtin_nontemporal_store(av[r], vc + dst);
       }
@@ -131,6 +180,16 @@ hipError_t gather_vpr(const Shape& sh, const void* q, const void* k, const void*
 }
 
 template <int VPR>
+hipError_t gather_by_rank_vpr(const Shape& sh, const void* k, const void* v, const int32_t* rank,
+                              void* kc, void* vc, hipStream_t st) {
+  dim3 grid((sh.L + kRowsByRank - 1) / kRowsByRank, sh.B * sh.Hkv);
+  gather_kv_by_rank<VPR><<<grid, kThreads, 0, st>>>(
+      static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), rank, static_cast<u32x4*>(kc),
+      static_cast<u32x4*>(vc), sh.Hq, sh.Hkv, sh.L, sh.L);
+  return hipGetLastError();
+}
+
+template <int VPR>
 hipError_t scatter_vpr(const Shape& sh, const void* oc, const int32_t* rank, void* o,
                        hipStream_t st) {
   dim3 grid((sh.L + kRowsScatter - 1) / kRowsScatter, sh.B * sh.Hq);
@@ -148,6 +207,16 @@ hipError_t launch_gather(const Shape& sh, const void* q, const void* k, const vo
     case 8: return gather_vpr<8>(sh, q, k, v, idx, budget, qc, kc, vc, st);
     case 16: return gather_vpr<16>(sh, q, k, v, idx, budget, qc, kc, vc, st);
     case 32: return gather_vpr<32>(sh, q, k, v, idx, budget, qc, kc, vc, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gather_kv_by_rank(const Shape& sh, const void* k, const void* v,
+                                    const int32_t* rank, void* kc, void* vc, hipStream_t st) {
+  switch (sh.row_bytes() / 16) {
+    case 8: return gather_by_rank_vpr<8>(sh, k, v, rank, kc, vc, st);
+    case 16: return gather_by_rank_vpr<16>(sh, k, v, rank, kc, vc, st);
+    case 32: return gather_by_rank_vpr<32>(sh, k, v, rank, kc, vc, st);
   }
   return hipErrorInvalidValue;
 }

@@ -304,20 +304,22 @@ __global__ __launch_bounds__(kMThreads) void score_mfma_rowstats(
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ks[buf][32 * kt + l32][16 * t + 8 * half]);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? zero : acc, 0, 0, 0);
         }
-        float x[16];
-        float tm = -INFINITY;
+        // Raw logits; c > 0, so the max of the scaled logits is the scaled max.
+        if (edge) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = j0 + 32 * kt + 8 * (e >> 2) + 4 * half + (e & 3);
-          x[e] = acc[e] * c;
-          if (edge && (key > (causal ? pos : L - 1) || r >= w)) x[e] = -INFINITY;
-          tm = fmaxf(tm, x[e]);
+          for (int e = 0; e < 16; ++e) {
+            const int key = j0 + 32 * kt + 8 * (e >> 2) + 4 * half + (e & 3);
+            if (key > (causal ? pos : L - 1) || r >= w) acc[e] = -INFINITY;
+          }
         }
-        const float mn = fmaxf(m, tm);
+        float tm = acc[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) tm = fmaxf(tm, acc[e]);
+        const float mn = fmaxf(m, tm * c);
         if (mn == -INFINITY) continue;        // nothing visible yet for this lane
         float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(x[e] - mn);
+        for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(fmaf(acc[e], c, -mn));
         z = z * __builtin_amdgcn_exp2f(m - mn) + sum;
         m = mn;
       }
@@ -403,12 +405,14 @@ __global__ __launch_bounds__(kMThreads) void score_mfma_colsum(
         }
         const int key = j0 + 32 * kt + l32;
         float csum = 0.f;
+        if (edge) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float p = __builtin_amdgcn_exp2f(fmaf(acc[v], c, -mrow[v])) * izrow[v];
-          if (edge && key > prow[v]) p = 0.f;
-          csum += p;
+          for (int v = 0; v < 16; ++v)
+            if (key > prow[v]) acc[v] = -INFINITY;
         }
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          csum = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[v], c, -mrow[v])), izrow[v], csum);
         csum += xhalf_other(csum);
         if (half == 0) cs_buf[unit * kScoreChunk + 32 * kt + l32] = csum;
       }

@@ -156,12 +156,26 @@ StepWs step_ws_layout(const Shape& s) {
   off = align256(off + sizeof(float) * 2 * size_t(s.B) * s.Hq * s.w * s.n_chunk());
   w.rowstat = off;
   off = align256(off + sizeof(float) * 2 * size_t(s.B) * s.Hq * s.w);
+  const size_t rows = size_t(s.bud_rows());
   w.sigma = off;
-  off = align256(off + sizeof(uint64_t) * size_t(s.bud_rows()) * s.L);
-  w.sigmax = off;
-  off = align256(off + sizeof(uint64_t) * size_t(s.bud_rows()));
-  w.selstate = off;
-  off = align256(off + sizeof(int32_t) * 4 * size_t(s.B) * s.Hq);
+  off = align256(off + sizeof(uint64_t) * rows * s.L);
+  w.bud_cand = off;
+  off = align256(off + sizeof(uint64_t) * rows * s.L);
+  w.bud_hcnt = off;                      // hcnt, hmass, ncand: contiguous (cleared together)
+  off = align256(off + sizeof(uint32_t) * rows * kBudgetLogBuckets);
+  w.bud_hmass = off;
+  off = align256(off + sizeof(uint64_t) * rows * kBudgetLogBuckets);
+  w.bud_ncand = off;
+  off = align256(off + sizeof(uint32_t) * rows);
+  w.bud_state = off;
+  off = align256(off + sizeof(uint64_t) * 4 * rows);
+  const size_t heads = size_t(s.B) * s.Hq;
+  w.sel_hist = off;
+  off = align256(off + sizeof(uint32_t) * 3 * heads * kSelectBuckets);
+  w.sel_state = off;
+  off = align256(off + sizeof(uint32_t) * 3 * heads * 2);
+  w.sel_cnt = off;
+  off = align256(off + sizeof(uint32_t) * heads * size_t(select_plan(s).nch) * 2);
   w.total = off;
   return w;
 }
@@ -280,6 +294,20 @@ tsa_status tsa_gather(const tsa_problem* prob, const void* q, const void* k, con
                   "tsa_gather");
 }
 
+tsa_status tsa_gather_kv(const tsa_problem* prob, const void* k, const void* v,
+                         const int32_t* rank, void* kc, void* vc, void* stream) {
+  tsa::Shape sh;
+  TSA_TRY(check_problem(prob, &sh));
+  TSA_TRY(check_ptr(k, "k"));
+  TSA_TRY(check_ptr(v, "v"));
+  TSA_TRY(check_ptr(rank, "rank"));
+  TSA_TRY(check_ptr(kc, "kc"));
+  TSA_TRY(check_ptr(vc, "vc"));
+  if (fault_injected()) return injected("tsa_gather_kv");
+  return launched(tsa::launch_gather_kv_by_rank(sh, k, v, rank, kc, vc, hipStream_t(stream)),
+                  "tsa_gather_kv");
+}
+
 tsa_status tsa_attention(const tsa_problem* prob, const void* q, const void* k, const void* v,
                          const int32_t* budget, int32_t kv_group, void* o, void* stream) {
   tsa::Shape sh;
@@ -360,10 +388,11 @@ tsa_status tsa_forward(const tsa_problem* prob, const void* q, const void* k, co
     return launched(err, "tsa_forward/budget");
   if ((err = tsa::launch_select(sh, scores, budget, idx, rank, base, st)) != hipSuccess)
     return launched(err, "tsa_forward/select");
-  // Compression of K and V; the attention reads Q and writes O through the
-  // index set, and the unselected rows are zeroed: the same bits as gather,
+  // Compression of K and V (each source row read once, written to every head
+  // that selected it); the attention reads Q and writes O through the index
+  // set, and the unselected rows are zeroed: the same bits as gather,
   // attention on the compact Q, K, V and scatter.
-  if ((err = tsa::launch_gather(sh, q, k, v, idx, budget, nullptr, kc, vc, st)) != hipSuccess)
+  if ((err = tsa::launch_gather_kv_by_rank(sh, k, v, rank, kc, vc, st)) != hipSuccess)
     return launched(err, "tsa_forward/gather");
   if ((err = tsa::launch_zero_unselected(sh, rank, o, st)) != hipSuccess)
     return launched(err, "tsa_forward/zero");

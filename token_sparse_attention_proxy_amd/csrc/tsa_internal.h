@@ -36,13 +36,31 @@ struct Shape {
   int n_chunk() const { return (L + kScoreChunk - 1) / kScoreChunk; }
 };
 
+constexpr int kBudgetLogBuckets = 4096;   // log-scale buckets of the budget's first pass
+constexpr int kSelectBuckets = 2048;      // digit buckets of the selection's histogram passes
+
+// Chunking of the selection: each head's candidates in `nch` chunks of
+// `chunk` tokens (one workgroup each); the compaction grid covers L in
+// `ngrid` chunks.
+struct SelectPlan {
+  int chunk, nch, ngrid;
+};
+SelectPlan select_plan(const Shape& s);
+
 // Step-scratch layout (offsets in bytes from the workspace base, 256-aligned).
+// R = budget rows (B, or B*Hq with per-head budgets).
 struct StepWs {
   size_t part;        // float2 [B*Hq*w*n_chunk]: per-chunk (max, sum) of each proxy row
   size_t rowstat;     // float2 [B*Hq*w]: (max in exp2 units, 1/Z) of each proxy row
-  size_t sigma;       // uint64 [R*L]: quantised masses (R = budget rows; head-summed if R = B)
-  size_t sigmax;      // uint64 [R]: max sigma per budget row
-  size_t selstate;    // int32 [B*Hq*4]: per-head selection threshold state
+  size_t sigma;       // uint64 [R*L]: quantised masses (head-summed if R = B)
+  size_t bud_cand;    // uint64 [R*L]: values of each row's crossing bucket
+  size_t bud_hcnt;    // uint32 [R*4096]: log-bucket counts   } cleared together:
+  size_t bud_hmass;   // uint64 [R*4096]: log-bucket masses   } contiguous, in
+  size_t bud_ncand;   // uint32 [R]: candidates per row       } this order
+  size_t bud_state;   // uint64 [R*4]: crossing bucket, mass and count below it, crossed
+  size_t sel_hist;    // uint32 [3*B*Hq*2048]: selection histograms, one per digit level
+  size_t sel_state;   // uint32 [3*B*Hq*2]: (prefix, count above) after each level's pick
+  size_t sel_cnt;     // uint32 [B*Hq*nch*2]: tokens above / equal to the threshold per chunk
   size_t total;
 };
 StepWs step_ws_layout(const Shape& s);
@@ -84,6 +102,10 @@ hipError_t launch_attention(const Shape& s, const void* q, const void* k, const 
 hipError_t launch_attention_qo(const Shape& s, const void* q, const void* kc, const void* vc,
                                const int32_t* budget, const int32_t* idx, void* o,
                                hipStream_t st);
+// K and V only, source-driven through the rank map: kc/vc[b,h,rank[b,h,j]] = K/V[b,g(h),j]
+// for every j with rank >= 0 (the same bytes as launch_gather with qc == nullptr).
+hipError_t launch_gather_kv_by_rank(const Shape& s, const void* k, const void* v,
+                                    const int32_t* rank, void* kc, void* vc, hipStream_t st);
 hipError_t launch_zero_unselected(const Shape& s, const int32_t* rank, void* o, hipStream_t st);
 hipError_t launch_scatter(const Shape& s, const void* oc, const int32_t* rank, void* o,
                           hipStream_t st);

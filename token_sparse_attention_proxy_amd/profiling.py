@@ -1,6 +1,6 @@
-"""HBM traffic of the attention kernel from rocprofv3 counters.
+"""HBM traffic of the kernels from rocprofv3 counters.
 
-Two sub-commands, meant to run under rocprofv3 and after it:
+Three sub-commands, meant to run under rocprofv3 and after it:
 
   python -m token_sparse_attention_proxy_amd.profiling run --workload NAME --path P
       Runs, in one process: a plain device-to-device copy of COPY_BYTES
@@ -11,7 +11,10 @@ Two sub-commands, meant to run under rocprofv3 and after it:
         fused: tsa_forward_fused on the workload's own seeded inputs (the
           indexed attention's reads follow the real index sets);
         forward: tsa_forward on the workload's own seeded inputs (its
-          attention reads Q and writes O through the real index sets).
+          attention reads Q and writes O through the real index sets);
+        all: tsa_forward, then the gather of Q, K and V and the scatter
+          entry points on the same index sets, so that every kernel of the
+          library's 128K op runs once on real data.
       Run it twice under ``rocprofv3 --pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``.
 
   python -m token_sparse_attention_proxy_amd.profiling summarize \\
@@ -21,6 +24,13 @@ Two sub-commands, meant to run under rocprofv3 and after it:
       device-to-device blit kernel), and records the attention
       kernel's HBM bytes per launch, keyed by the kernel source hash, so that
       bench.py reports them only while the kernel is unchanged.
+
+  python -m token_sparse_attention_proxy_amd.profiling summarize-all \\
+        --fetch DIR --write DIR --workload NAME [--out profiles/traffic.json]
+      The same for every kernel of the library found in the two runs of
+      ``run --path all``: the mean counter bytes per dispatch, scaled by the
+      copy, keyed by kernel and by the hash of the source file it is built
+      from.
 """
 from __future__ import annotations
 
@@ -38,6 +48,36 @@ COPY_BYTES = 1 << 30
 # template arguments (IDX, BS, QO) of the attention kernel each path runs
 KERNEL_ARGS = {"compact": "false, false, false", "fused": "true, false, false",
                "forward": "false, false, true"}
+CSRC = os.path.join(ROOT, "token_sparse_attention_proxy_amd", "csrc")
+# source file of each kernel family (the hash keys the recorded counters)
+KERNEL_SOURCES = {"score_": "score.hip", "budget_": "budget.hip", "clear_u64": "budget.hip",
+                  "select_": "select.hip", "gather_rows": "gather_scatter.hip",
+                  "scatter_rows": "gather_scatter.hip", "zero_rows": "gather_scatter.hip",
+                  "attn_fwd": "attention.hip"}
+
+
+def kernel_source(kname: str):
+    for prefix, src in KERNEL_SOURCES.items():
+        if kname.startswith(prefix):
+            return os.path.join(CSRC, src)
+    return None
+
+
+def short_name(full: str) -> str:
+    """'void tsa::(anonymous namespace)::gather_rows<16, false, 128>(...)' -> 'gather_rows<16, false, 128>'."""
+    name = full.strip().replace("(anonymous namespace)", "anon")
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, ch in enumerate(name):          # the argument list: the first '(' outside <>
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            name = name[:i]
+            break
+    return name.split("::")[-1]
 
 
 def source_sha(path: str = ATTN_SRC) -> str:
@@ -53,7 +93,7 @@ def cmd_run(args):
 
     wl = inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    if args.path in ("fused", "forward"):
+    if args.path in ("fused", "forward", "all"):
         q, k, v = inputs.make_qkv(wl)
         tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
         qd, kd, vd = (torch.from_numpy(x).to(tdt).to(dev) for x in (q, k, v))
@@ -64,6 +104,18 @@ def cmd_run(args):
     torch.cuda.synchronize()
     del src, dst
     prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, wl.taus[0], wl.dtype)
+    if args.path == "all":
+        o, bud, idx = T.tsa_forward(prob, qd, kd, vd)
+        s = torch.empty((wl.B, wl.Hq, wl.L), dtype=torch.float32, device=dev)
+        _, rank = T.tsa_select(prob, T.tsa_score(prob, qd, kd, s), bud)
+        qc, kc, vc = T.tsa_gather(prob, qd, kd, vd, idx, bud)
+        del qc, kc, vc
+        oc = torch.zeros_like(o)
+        T.tsa_scatter(prob, oc, rank, o)
+        torch.cuda.synchronize()
+        print(f"ran copy of {COPY_BYTES} B, tsa_forward, score, select, gather and scatter on "
+              f"{wl.name}, budget {bud.cpu().tolist()}")
+        return
     if args.path in ("fused", "forward"):
         run = T.tsa_forward_fused if args.path == "fused" else T.tsa_forward
         o, bud, _ = run(prob, qd, kd, vd)
@@ -133,13 +185,49 @@ def cmd_summarize(args):
     print(json.dumps(entry, indent=1))
 
 
+def _per_kernel(rows):
+    """{short kernel name: mean counter KiB per dispatch, dispatches}."""
+    acc = {}
+    for full, val in rows:
+        n = short_name(full)
+        tot, cnt = acc.get(n, (0.0, 0))
+        acc[n] = (tot + val, cnt + 1)
+    return {n: (tot / cnt, cnt) for n, (tot, cnt) in acc.items()}
+
+
+def cmd_summarize_all(args):
+    fetch = _read(args.fetch, "FETCH_SIZE")
+    write = _read(args.write, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (max(_pick(fetch, "copyBuffer")) * 1024.0)
+    w_scale = COPY_BYTES / (max(_pick(write, "copyBuffer")) * 1024.0)
+    pf, pw = _per_kernel(fetch), _per_kernel(write)
+    tab = {}
+    if os.path.exists(args.out):
+        with open(args.out) as f:
+            tab = json.load(f)
+    for n in sorted(pf):
+        src = kernel_source(n)
+        if src is None or n not in pw:
+            continue
+        fb = pf[n][0] * 1024.0 * f_scale
+        wb = pw[n][0] * 1024.0 * w_scale
+        entry = {"source_sha": source_sha(src), "source": os.path.basename(src), "path": "all",
+                 "dispatches": pf[n][1], "fetch_bytes_per_launch": fb,
+                 "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
+                 "fetch_scale": f_scale, "write_scale": w_scale, "copy_bytes": COPY_BYTES}
+        tab.setdefault(n, {})[args.workload] = entry
+        print(f"{n:45s} x{pf[n][1]:3d}  fetch {fb / 1e6:10.2f} MB  write {wb / 1e6:10.2f} MB")
+    with open(args.out, "w") as f:
+        json.dump(tab, f, indent=1, sort_keys=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
     r.add_argument("--workload", default="llama8b_bf16_L128k")
     r.add_argument("--budget", type=int, default=123997)
-    r.add_argument("--path", choices=sorted(KERNEL_ARGS), default="fused")
+    r.add_argument("--path", choices=sorted(KERNEL_ARGS) + ["all"], default="fused")
     r.set_defaults(fn=cmd_run)
     s = sub.add_parser("summarize")
     s.add_argument("--fetch", required=True)
@@ -150,6 +238,12 @@ def main():
     s.add_argument("--d", type=int, default=128)
     s.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
     s.set_defaults(fn=cmd_summarize)
+    a = sub.add_parser("summarize-all")
+    a.add_argument("--fetch", required=True)
+    a.add_argument("--write", required=True)
+    a.add_argument("--workload", default="llama8b_bf16_L128k")
+    a.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    a.set_defaults(fn=cmd_summarize_all)
     args = ap.parse_args()
     args.fn(args)
 

@@ -189,6 +189,23 @@ def tsa_gather(prob: Problem, q, k, v, idx, budget, qc=None, kc=None, vc=None, w
     return (qc if with_q else None), kc, vc
 
 
+def tsa_gather_kv(prob: Problem, k, v, rank, kc=None, vc=None):
+    """K and V only, source-driven through the rank map (tsa_forward's gather)."""
+    lib = _lib.load()
+    p = prob.c()
+    shape = _heads(prob, prob.Hq)
+    kc = _empty(shape, k.dtype, k) if kc is None else kc
+    vc = _empty(shape, k.dtype, k) if vc is None else vc
+    _expect("k", k, _heads(prob, prob.Hkv), prob.torch_dtype)
+    _expect("v", v, _heads(prob, prob.Hkv), prob.torch_dtype)
+    _check_rows(prob, rank=rank)
+    _expect("kc", kc, shape, prob.torch_dtype)
+    _expect("vc", vc, shape, prob.torch_dtype)
+    check(lib.tsa_gather_kv(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(rank), _ptr(kc), _ptr(vc),
+                            _stream(k.device)), "tsa_gather_kv")
+    return kc, vc
+
+
 def tsa_attention(prob: Problem, q, k, v, budget=None, kv_group: int = 1, o=None):
     lib = _lib.load()
     p = prob.c()
@@ -321,6 +338,7 @@ def forward(q, k, v, w: int, tau: float, fused: bool = False, flags: int = 0):
 
 __all__ = ["Problem", "TsaError", "workspace_bytes", "forward_workspace_bytes",
            "fused_workspace_bytes", "tsa_score", "tsa_budget", "tsa_select", "tsa_gather",
+           "tsa_gather_kv",
            "tsa_attention", "tsa_scatter", "tsa_forward", "tsa_attention_indexed",
            "tsa_forward_fused", "tsa_zero_unselected", "block_mask_words",
            "tsa_attention_block_sparse", "forward", "TSA_FLAG_NONCAUSAL_PROXY",
