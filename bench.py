@@ -241,6 +241,18 @@ def measured_traffic(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
+def full_oracle_small():
+    """The whole fp64 oracle forward, unsampled, on the 1K fp32 workload (B=1, Hq=Hkv=4,
+    L=1024, d=64, w=16): the one configuration small enough to time in full here."""
+    from oracle import tsa_oracle as O
+    from token_sparse_attention_proxy_amd import inputs
+    wl = inputs.WORKLOADS["tiny_mha_f32_L1k"]
+    q, k, v = inputs.make_qkv(wl)
+    t0 = time.perf_counter()
+    O.forward(q, k, v, wl.w, wl.taus[0])
+    return {"workload": wl.name, "ms_per_layer": round((time.perf_counter() - t0) * 1e3, 1)}
+
+
 def cpu_baseline(wl, q, k, v, tau, K_gpu: int):
     """The fp64 oracle, as it stands, on a bounded sample; scaled to ms/layer."""
     from threadpoolctl import threadpool_info
@@ -295,6 +307,7 @@ def cpu_baseline(wl, q, k, v, tau, K_gpu: int):
         "measured_s": round(t_score + t_budget + t_select / (B * Hq) + t_gather / (B * Hq)
                             + t_attn_sample + t_scatter / (B * Hq), 2),
         "budget_matches_gpu": bool(int(budget[0]) == K_gpu),
+        "full_oracle_small": full_oracle_small(),
         "host": host,
     }
 

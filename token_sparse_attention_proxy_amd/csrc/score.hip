@@ -293,36 +293,44 @@ __global__ __launch_bounds__(kMThreads) void score_mfma_rowstats(
       if (!own) load_q_tile<D>(q + int64_t(bh) * L * D, L, w, r0, qf);
       const int r = r0 + l32;                 // this lane's proxy row
       const int pos = L - w + r;              // its sequence position
-      float m = -INFINITY, z = 0.f;
-      // Not unrolled: the rolled loop keeps the register count low enough
-      // for two workgroups per CU.
+      // One loop for the chunks that need no mask and one for the edge
+      // chunks, so the interior loop carries no compare or select.
+      auto walk = [&](auto edge_c) {
+        constexpr bool EDGE = decltype(edge_c)::value;
+        float m = -INFINITY, z = 0.f;
+        // Not unrolled: the rolled loop keeps the register count low enough
+        // for two workgroups per CU.
 #pragma unroll 1
-      for (int kt = 0; kt < kScoreChunk / 32; ++kt) {
-        f32x16 acc;
+        for (int kt = 0; kt < kScoreChunk / 32; ++kt) {
+          f32x16 acc;
 #pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ks[buf][32 * kt + l32][16 * t + 8 * half]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? zero : acc, 0, 0, 0);
-        }
-        // Raw logits; c > 0, so the max of the scaled logits is the scaled max.
-        if (edge) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = j0 + 32 * kt + 8 * (e >> 2) + 4 * half + (e & 3);
-            if (key > (causal ? pos : L - 1) || r >= w) acc[e] = -INFINITY;
+          for (int t = 0; t < KS; ++t) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ks[buf][32 * kt + l32][16 * t + 8 * half]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], t == 0 ? zero : acc, 0, 0, 0);
           }
+          // Raw logits; c > 0, so the max of the scaled logits is the scaled max.
+          if constexpr (EDGE) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int key = j0 + 32 * kt + 8 * (e >> 2) + 4 * half + (e & 3);
+              if (key > (causal ? pos : L - 1) || r >= w) acc[e] = -INFINITY;
+            }
+          }
+          float tm = acc[0];
+#pragma unroll
+          for (int e = 1; e < 16; ++e) tm = fmaxf(tm, acc[e]);
+          const float mn = fmaxf(m, tm * c);
+          if (mn == -INFINITY) continue;      // nothing visible yet for this lane
+          float sum = 0.f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(fmaf(acc[e], c, -mn));
+          z = z * __builtin_amdgcn_exp2f(m - mn) + sum;
+          m = mn;
         }
-        float tm = acc[0];
-#pragma unroll
-        for (int e = 1; e < 16; ++e) tm = fmaxf(tm, acc[e]);
-        const float mn = fmaxf(m, tm * c);
-        if (mn == -INFINITY) continue;        // nothing visible yet for this lane
-        float sum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(fmaf(acc[e], c, -mn));
-        z = z * __builtin_amdgcn_exp2f(m - mn) + sum;
-        m = mn;
-      }
+        return make_float2(m, z);
+      };
+      const float2 mz = edge ? walk(std::true_type{}) : walk(std::false_type{});
+      const float m = mz.x, z = mz.y;
       // combine the two lane halves, which saw different keys of the same row
       const float mo = xhalf_other(m), zo = xhalf_other(z);
       const float M = fmaxf(m, mo);
@@ -393,29 +401,40 @@ __global__ __launch_bounds__(kMThreads) void score_mfma_colsum(
     const bool edge = causal && j0 + kScoreChunk - 1 > L - w;
     for (int unit = wave; unit < units; unit += kMWaves) {
       if (!own) load_unit(unit);
-      // Not unrolled: the rolled loop keeps the register count low enough
-      // for two workgroups per CU.
+      // One loop for the chunks that need no mask and one for the edge
+      // chunks, so the interior loop carries no compare or select.
+      auto walk = [&](auto edge_c) {
+        constexpr bool EDGE = decltype(edge_c)::value;
+        // Not unrolled: the rolled loop keeps the register count low enough
+        // for two workgroups per CU.
 #pragma unroll 1
-      for (int kt = 0; kt < kScoreChunk / 32; ++kt) {
-        f32x16 acc;
+        for (int kt = 0; kt < kScoreChunk / 32; ++kt) {
+          f32x16 acc;
 #pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&ks[buf][32 * kt + l32][16 * t + 8 * half]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t], bk, t == 0 ? zero : acc, 0, 0, 0);
+          for (int t = 0; t < KS; ++t) {
+            const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&ks[buf][32 * kt + l32][16 * t + 8 * half]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t], bk, t == 0 ? zero : acc, 0, 0, 0);
+          }
+          if constexpr (EDGE) {
+            const int key = j0 + 32 * kt + l32;
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (key > prow[v]) acc[v] = -INFINITY;
+          }
+          // two independent sums of the rows this lane holds, added at the end
+          float cs0 = 0.f, cs1 = 0.f;
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {
+            cs0 = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[v], c, -mrow[v])), izrow[v], cs0);
+            cs1 = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[v + 1], c, -mrow[v + 1])), izrow[v + 1], cs1);
+          }
+          float csum = cs0 + cs1;
+          csum += xhalf_other(csum);
+          if (half == 0) cs_buf[unit * kScoreChunk + 32 * kt + l32] = csum;
         }
-        const int key = j0 + 32 * kt + l32;
-        float csum = 0.f;
-        if (edge) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (key > prow[v]) acc[v] = -INFINITY;
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          csum = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[v], c, -mrow[v])), izrow[v], csum);
-        csum += xhalf_other(csum);
-        if (half == 0) cs_buf[unit * kScoreChunk + 32 * kt + l32] = csum;
-      }
+      };
+      if (edge) walk(std::true_type{});
+      else walk(std::false_type{});
     }
     if (ch + 1 < ch1) kc.store(ks[buf ^ 1]);
     __syncthreads();
