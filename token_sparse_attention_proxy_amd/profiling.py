@@ -50,10 +50,10 @@ KERNEL_ARGS = {"compact": "false, false, false", "fused": "true, false, false",
                "forward": "false, false, true"}
 CSRC = os.path.join(ROOT, "token_sparse_attention_proxy_amd", "csrc")
 # source file of each kernel family (the hash keys the recorded counters)
-KERNEL_SOURCES = {"score_": "score.hip", "budget_": "budget.hip", "clear_u64": "budget.hip",
-                  "select_": "select.hip", "gather_rows": "gather_scatter.hip",
-                  "scatter_rows": "gather_scatter.hip", "zero_rows": "gather_scatter.hip",
-                  "attn_fwd": "attention.hip"}
+KERNEL_SOURCES = {"score_": "score.hip", "budget_": "budget.hip", "clear_words": "budget.hip",
+                  "sel_": "select.hip", "gather_rows": "gather_scatter.hip",
+                  "gather_kv_by_rank": "gather_scatter.hip", "scatter_rows": "gather_scatter.hip",
+                  "zero_rows": "gather_scatter.hip", "attn_fwd": "attention.hip"}
 
 
 def kernel_source(kname: str):
