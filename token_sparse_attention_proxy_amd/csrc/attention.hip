@@ -26,15 +26,18 @@
 //     an accumulator holding -m, so the subtraction costs nothing, and the
 //     loop needs no running max, no cross-lane reduction and no rescaling
 //     of O, which stays in accumulator registers touched only by MFMA: one
-//     exp2, half a bf16 pack and half a dot2 (the row sum) per score.
+//     exp2, half a bf16 pack and one fp32 add (the row sum) per score.
+//     (Row sums as bf16 dot2 against (1, 1) would take half the
+//     instructions, but v_dot2 does not overlap MFMA issue on gfx950 the
+//     way plain fp32 VALU does.)
 //     Softmax is invariant to the reference, so the result equals the usual
 //     one up to rounding.
 //     A row sum above 2^64 (a later logit far above the first tile's max)
 //     makes the workgroup recompute with the exact row max as reference, so
 //     nothing can overflow;
-//   * P rounded to bf16 for the PV product, row sums of that rounded P (so
-//     the weights applied to V sum to one), fp32 output accumulators, final
-//     division and round-to-nearest-even to bf16;
+//   * P rounded to bf16 for the PV product, fp32 row sums of the unrounded
+//     P, fp32 output accumulators, final division and round-to-nearest-even
+//     to bf16;
 //   * loads and stores go through buffer resources sized to the n valid
 //     rows: out-of-range rows read as 0 and are never written, without
 //     branches;
@@ -85,13 +88,6 @@ __device__ __forceinline__ float max_halves(float x) {
 __device__ __forceinline__ float sum_halves(float x) {
   auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-// acc + the two bf16 halves of w (one dot2 against (1, 1))
-__device__ __forceinline__ float add_pair(float acc, uint32_t w) {
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, acc, false);
 }
 
 template <int D, int NBUF>
@@ -316,8 +312,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   float l_run = 0.f;      // this lane's share of the row sum
 
   // P = exp2(S - m_ref) (biased: S^T already holds -m_ref from its chain start),
-  // rounded to bf16; row sums of the rounded P (a dot2 of each packed pair
-  // against (1, 1)), then O^T += V^T P^T.
+  // rounded to bf16; fp32 row sums of P (four partial sums), then O^T += V^T P^T.
   auto pv = [&](int buf, const f32x16 (&sacc)[NSUB], bool biased) {
     const float mneg = biased ? 0.f : -m_ref;
     bf16x8 pb[NSUB * 2];
@@ -332,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
           const float p0 = __builtin_amdgcn_exp2f(sacc[sb][8 * tt + 2 * e2] + mneg);
           const float p1 = __builtin_amdgcn_exp2f(sacc[sb][8 * tt + 2 * e2 + 1] + mneg);
           pk[e2] = pack_bf16x2(p0, p1);
-          ls[e2] = add_pair(ls[e2], pk[e2]);
+          ls[e2] += p0 + p1;
         }
         pb[2 * sb + tt] = __builtin_bit_cast(bf16x8, pk);
       }
@@ -349,9 +344,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
   // The same tile as qk + pv (same operations in the same accumulation
   // orders, so the same bits) for tiles below the diagonal, written as one
   // software pipeline in program order: LDS operand reads run PF ahead of
-  // their MFMA, the S^T chain of subtile q+1 carries the exp/convert work of
-  // subtile q, the PV MFMAs of the first subtiles carry that of the last, and
-  // the remaining PV MFMAs carry the row sums.
+  // their MFMA, the S^T chain of subtile q+1 carries the exp/convert/row-sum
+  // work of subtile q, and the PV MFMAs of the first subtiles carry that of
+  // the last.
   auto hot = [&](int buf) {
     constexpr int NQK = NSUB * KS;            // S^T MFMAs, chain after chain
     constexpr int NPV = 2 * NSUB * DT;        // O^T MFMAs, kk-major
@@ -376,6 +371,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
       const float p0 = __builtin_amdgcn_exp2f(sacc[sb][2 * p]);
       const float p1 = __builtin_amdgcn_exp2f(sacc[sb][2 * p + 1]);
       pk[2 * sb + p / 4][p % 4] = pack_bf16x2(p0, p1);
+      ls[p % 4] += p0 + p1;
     };
     bf16x8 ring[PF + 1];
 #pragma unroll
@@ -398,15 +394,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
         if (j < LAST_SLOT) {
 #pragma unroll
           for (int p = j * LPP; p < (j + 1) * LPP && p < 8; ++p) softmax_pair(LAST, p);
-        } else {
-          // Row sums of the packed P, in the PV MFMAs that carry no softmax.
-          constexpr int NPK = 8 * NSUB;        // packed words of this tile's P
-          constexpr int SPAN = NPV - LAST_SLOT;
-          constexpr int PER = (NPK + SPAN - 1) / SPAN;
-          const int jj = j - LAST_SLOT;
-#pragma unroll
-          for (int w2 = jj * PER; w2 < (jj + 1) * PER && w2 < NPK; ++w2)
-            ls[w2 & 3] = add_pair(ls[w2 & 3], pk[w2 / 4][w2 % 4]);
         }
       }
     }
