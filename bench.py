@@ -14,7 +14,9 @@ Printed as one JSON line, with:
     no selection) and the speedup against it;
   * a per-kernel breakdown of both paths timed with HIP events on the launch
     stream, and the roofline of the dominant kernel (the attention of the
-    timed path) from those launches;
+    timed path) from those launches, beside the sustained rate of a bare bf16
+    MFMA loop on the same GPU with random and with constant operands (the
+    chip's clock depends on how much the operands toggle);
   * the fp64 CPU oracle timed on a bounded sample of the same workload;
   * the alternative readings (TSA_FLAG_* bits): K/L and ms per layer of the
     timed path under each, against the same dense baseline;
@@ -241,6 +243,32 @@ def measured_traffic(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
+def mfma_ceiling(st, iters: int = 60000, reps: int = 2):
+    """Sustained bf16 MFMA rate of a register-only loop (two waves per SIMD, four
+    accumulator chains), with random and with constant operands; best of reps launches
+    of about 30-50 ms each, timed with HIP events on the launch stream."""
+    import torch
+    from token_sparse_attention_proxy_amd import tsa as T
+    sink = torch.empty(T.probe_sink_bytes() // 4, dtype=torch.float32, device="cuda")
+    res = {}
+    for key, rnd in (("random_operands", True), ("constant_operands", False)):
+        T.probe_mfma_bf16(rnd, 100, sink)
+        best = 0.0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fl = T.probe_mfma_bf16(rnd, iters, sink)
+            e1.record(st)
+            torch.cuda.synchronize()
+            best = max(best, fl / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        res[key] = round(best, 1)
+    assert bool(torch.isfinite(sink).all()), "probe accumulators not finite"
+    res["unit"] = "TFLOP/s"
+    res["what"] = ("v_mfma_f32_32x32x16_bf16 loop, operands in registers, 2 waves/SIMD, "
+                   "one workgroup per CU; random: random signs/mantissas, magnitudes in [0.25, 2)")
+    return res
+
+
 def full_oracle_small():
     """The whole fp64 oracle forward, unsampled, on the 1K fp32 workload (B=1, Hq=Hkv=4,
     L=1024, d=64, w=16): the one configuration small enough to time in full here."""
@@ -424,6 +452,13 @@ def main():
     steps_ms = {n: float(np.mean(per_rep[n])) for n in names}
     log("[bench] kernels ms: " + ", ".join(f"{n} {steps_ms[n]:.3f}" for n in steps_ms))
 
+    # ---- the bf16 MFMA ceiling on this GPU, right after the attention launches: a
+    # register-only MFMA loop with random and with constant operands (include/tsa_probe.h)
+    ceiling = mfma_ceiling(st) if wl.dtype == "bf16" else None
+    if ceiling:
+        log(f"[bench] MFMA ceiling: random operands {ceiling['random_operands']} TFLOP/s, "
+            f"constant operands {ceiling['constant_operands']} TFLOP/s")
+
     # ---- dense causal attention baseline (same kernel, GQA head map)
     dense_ms = None
     if not args.no_dense:
@@ -554,6 +589,9 @@ def main():
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic, "kernel": kname,
                 "flops_per_launch": flops, "avg_launch_ms": round(steps_ms[attn_step], 4)}
+    if ceiling:
+        ceiling["attention_frac_of_random"] = round(achieved / ceiling["random_operands"], 4)
+        roofline["mfma_ceiling"] = ceiling
 
     # HBM fractions of the byte-moving steps (algorithmic bytes)
     eb = 2 if bf16 else 4

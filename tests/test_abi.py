@@ -251,3 +251,27 @@ def test_score_tile_bound(lib, monkeypatch):
     assert score(Hq=64, Hkv=1, L=4096, w=92 * 32 + 1) == _lib.TSA_ERR_UNSUPPORTED
     assert score(Hq=4, Hkv=1, L=4096, w=92 * 32 + 1, dtype=_lib.TSA_F32) == _lib.TSA_ERR_HIP
     assert score(Hq=2, Hkv=2, L=4096, w=4096, dtype=_lib.TSA_F32) == _lib.TSA_ERR_HIP
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "tsa_probe.h")
+
+
+def test_probe_library_exports_its_header():
+    if not os.path.exists(_lib.PROBE_PATH):
+        from token_sparse_attention_proxy_amd import build
+        build.build()
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    syms = sorted(set(re.findall(r"\b(tsa_[a-z_0-9]+)\s*\(", text)))
+    assert set(syms) == set(_lib.PROBE_EXPORTS), syms
+    probe = _lib.load_probe()
+    for name in syms:
+        assert hasattr(probe, name), name
+
+
+def test_probe_rejects_bad_arguments_without_launching():
+    probe = _lib.load_probe()
+    flops = ctypes.c_double(0.0)
+    # null sink, null flops, iters < 1: rejected before any device query or launch
+    assert probe.tsa_probe_mfma_bf16(1, 10, None, 1 << 20, ctypes.byref(flops), None) == 1
+    assert probe.tsa_probe_mfma_bf16(1, 10, FAKE, 1 << 20, None, None) == 1
+    assert probe.tsa_probe_mfma_bf16(1, 0, FAKE, 1 << 20, ctypes.byref(flops), None) == 1

@@ -10,6 +10,7 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libtsa.so")
+PROBE_PATH = os.path.join(PKG, "libtsa_probe.so")
 
 TSA_OK, TSA_ERR_INVALID_ARG, TSA_ERR_UNSUPPORTED, TSA_ERR_WORKSPACE, TSA_ERR_HIP = range(5)
 TSA_F32, TSA_BF16 = 0, 1
@@ -78,6 +79,32 @@ def load() -> ctypes.CDLL:
             fn.argtypes = args
         _lib = lib
     return _lib
+
+
+# include/tsa_probe.h: the bf16 MFMA ceiling probe, a library of its own.
+PROBE_EXPORTS = ["tsa_probe_sink_bytes", "tsa_probe_mfma_bf16"]
+_PROBE_SIGNATURES = {
+    "tsa_probe_sink_bytes": (_sz, []),
+    "tsa_probe_mfma_bf16": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _vp, _sz,
+                                           ctypes.POINTER(ctypes.c_double), _vp]),
+}
+_probe = None
+
+
+def load_probe() -> ctypes.CDLL:
+    """Load libtsa_probe.so once; raise if it is missing."""
+    global _probe
+    if _probe is None:
+        if not os.path.exists(PROBE_PATH):
+            raise RuntimeError(
+                f"{PROBE_PATH} is not built; run `python -m token_sparse_attention_proxy_amd.build`")
+        lib = ctypes.CDLL(PROBE_PATH)
+        for name, (res, args) in _PROBE_SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _probe = lib
+    return _probe
 
 
 class TsaError(RuntimeError):

@@ -16,9 +16,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtsa.so")
+PROBE_LIB = os.path.join(PKG, "libtsa_probe.so")   # the MFMA ceiling probe (include/tsa_probe.h)
 
 SOURCES = ["tsa_api.cpp", "score.hip", "budget.hip", "select.hip", "gather_scatter.hip",
            "attention.hip"]
+PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -40,18 +42,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -343,3 +343,21 @@ __all__ = ["Problem", "TsaError", "workspace_bytes", "forward_workspace_bytes",
            "tsa_forward_fused", "tsa_zero_unselected", "block_mask_words",
            "tsa_attention_block_sparse", "forward", "TSA_FLAG_NONCAUSAL_PROXY",
            "TSA_FLAG_PER_HEAD_BUDGET", "TSA_FLAG_KEEP_WINDOW"]
+
+
+# ---------------------------------------------------------------- measurement probe
+def probe_sink_bytes() -> int:
+    return int(_lib.load_probe().tsa_probe_sink_bytes())
+
+
+def probe_mfma_bf16(random_operands: bool, iters: int, sink: torch.Tensor) -> float:
+    """Enqueue the bf16 MFMA ceiling probe (include/tsa_probe.h) on the current stream;
+    returns the launch's MFMA FLOPs.  sink: a device tensor of probe_sink_bytes() bytes."""
+    lib = _lib.load_probe()
+    flops = ctypes.c_double(0.0)
+    rc = lib.tsa_probe_mfma_bf16(int(bool(random_operands)), int(iters), _ptr(sink),
+                                 sink.numel() * sink.element_size(), ctypes.byref(flops),
+                                 _stream(sink.device))
+    if rc != 0:
+        raise RuntimeError(f"tsa_probe_mfma_bf16 failed with status {rc}")
+    return flops.value
