@@ -619,19 +619,9 @@ def main():
                    "algorithmic_bytes": int(hbm_bytes[n])} for n in hbm_bytes}
     # HBM bytes from rocprofv3 FETCH_SIZE + WRITE_SIZE of the same kernel sources (null when a
     # source changed since they were recorded), and their ratio to the algorithmic bytes
-    vpr = wl.d * eb // 16
-    step_kernels = {
-        "score": [f"score_mfma_rowstats<{wl.d}>", "score_merge", f"score_mfma_colsum<{wl.d}>"],
-        "budget": ["clear_words", "budget_sigma", "budget_extract", "budget_cut"],
-        "select": ["sel_clear", "sel_level<0>", "sel_level<1>", "sel_level<2>", "sel_count",
-                   "sel_compact"],
-        "gather": [f"gather_rows<{vpr}, true, 32>"],
-        "gather_kv": [f"gather_kv_by_rank<{vpr}>"],
-        "scatter": [f"scatter_rows<{vpr}>"],
-        "zero_fill": [f"zero_rows<{vpr}>"],
-    }
+    from token_sparse_attention_proxy_amd.profiling import step_kernels
     traffic_tab = load_traffic()
-    for n, kns in step_kernels.items():
+    for n, kns in step_kernels(wl.d, wl.d * eb // 16).items():
         cb = counter_bytes(traffic_tab, kns, wl.name) if bf16 else None
         kernels[n]["counter_bytes"] = None if cb is None else int(cb)
         kernels[n]["counter_over_algorithmic"] = None if cb is None else round(cb / hbm_bytes[n], 3)

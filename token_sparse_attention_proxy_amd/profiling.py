@@ -56,6 +56,21 @@ KERNEL_SOURCES = {"score_": "score.hip", "budget_": "budget.hip", "clear_words":
                   "zero_rows": "gather_scatter.hip", "attn_fwd": "attention.hip"}
 
 
+def step_kernels(d: int, vpr: int) -> dict:
+    """Kernels of each step of the op (short names), for head dimension d and vpr 16-byte
+    vectors per row."""
+    return {
+        "score": [f"score_mfma_rowstats<{d}>", "score_merge", f"score_mfma_colsum<{d}>"],
+        "budget": ["clear_words", "budget_sigma", "budget_extract", "budget_cut"],
+        "select": ["sel_clear", "sel_level<0>", "sel_level<1>", "sel_level<2>", "sel_count",
+                   "sel_compact"],
+        "gather": [f"gather_rows<{vpr}, true, 32>"],
+        "gather_kv": [f"gather_kv_by_rank<{vpr}>"],
+        "scatter": [f"scatter_rows<{vpr}>"],
+        "zero_fill": [f"zero_rows<{vpr}>"],
+    }
+
+
 def kernel_source(kname: str):
     for prefix, src in KERNEL_SOURCES.items():
         if kname.startswith(prefix):
@@ -221,6 +236,251 @@ def cmd_summarize_all(args):
         json.dump(tab, f, indent=1, sort_keys=True)
 
 
+# ---------------------------------------------------------------- markdown summaries
+def _bench_line(path):
+    """The JSON line a bench.py run printed (its last line that parses)."""
+    line = None
+    for ln in open(path):
+        ln = ln.strip()
+        if ln.startswith("{"):
+            try:
+                line = json.loads(ln)
+            except ValueError:
+                pass
+    if line is None:
+        raise SystemExit(f"no bench JSON line in {path}")
+    return line
+
+
+def _first(dirpath, pattern):
+    got = sorted(glob.glob(os.path.join(dirpath, "**", pattern), recursive=True))
+    if not got:
+        raise SystemExit(f"no {pattern} under {dirpath}")
+    return got[0]
+
+
+def _shape_header(wl_name):
+    sys.path.insert(0, ROOT)
+    from token_sparse_attention_proxy_amd import inputs
+    wl = inputs.WORKLOADS[wl_name]
+    return wl, (f"{wl.name}: B={wl.B}, Hq={wl.Hq}, Hkv={wl.Hkv}, L={wl.L}, d={wl.d}, "
+                f"w={wl.w}, tau={wl.taus[0]}")
+
+
+def cmd_trace_summary(args):
+    """Kernel trace of a bench.py run: per-kernel statistics of the headline workload's
+    dispatches (those before the end of the last dense attention launch on that shape;
+    the parity check and the sweep that follow use other shapes)."""
+    wl, hdr = _shape_header(args.workload)
+    bench = _bench_line(args.bench)
+    rows = list(csv.DictReader(open(_first(args.trace, "*kernel_trace.csv"))))
+    gx = (wl.L + 255) // 256 * 512
+    dense = [r for r in rows if short_name(r["Kernel_Name"]) == f"attn_fwd_bf16<{wl.d}, false, false, false>"
+             and int(r["Grid_Size_X"]) == gx and int(r["Grid_Size_Y"]) == wl.B * wl.Hq]
+    if not dense:
+        raise SystemExit("no dense attention launch of the headline shape in the trace")
+    end = max(int(r["End_Timestamp"]) for r in dense)
+    per = {}
+    for r in rows:
+        n = short_name(r["Kernel_Name"])
+        if int(r["Start_Timestamp"]) > end or (kernel_source(n) is None and
+                                               not n.startswith("mfma_probe")):
+            continue             # torch's own kernels (input copies, fills) are left out
+        per.setdefault(short_name(r["Kernel_Name"]), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+    total = sum(sum(v) for v in per.values())
+    out = [f"# Kernel trace: bench.py on the {wl.L // 1024}K workload ({hdr})", "",
+           "Command (from the repository root `$R`, on one MI355X):", "", "```",
+           args.command, "```", "",
+           "Per-kernel durations of every dispatch of the headline workload in that run (the "
+           "timed steps, the other path, the per-kernel breakdown, the MFMA ceiling probe and "
+           "the dense baseline; the parity check and the sweep that follow are left out, and so "
+           "are torch's own kernels). `*_kernel_stats.csv` of the same run holds all "
+           "dispatches.", "",
+           f"The bench line of this run: {bench['value']} ms per layer; "
+           f"`roofline.avg_launch_ms` = {bench['roofline']['avg_launch_ms']} ms for "
+           f"`{bench['roofline']['kernel']}`, {bench['roofline']['achieved']} TFLOP/s, "
+           f"frac {bench['roofline']['frac']}."]
+    ceil = bench["roofline"].get("mfma_ceiling")
+    if ceil:
+        out.append(f"MFMA ceiling probe in the same run: {ceil['random_operands']} TFLOP/s with "
+                   f"random operands, {ceil['constant_operands']} with constant operands; the "
+                   f"attention is at {ceil['attention_frac_of_random']} of the random-operand rate.")
+    out += ["", "| kernel | calls | avg ms | min ms | max ms | share |", "|---|---|---|---|---|---|"]
+    for n, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| `{n}` | {len(v)} | {sum(v) / len(v):.4f} | {min(v):.4f} | {max(v):.4f} | "
+                   f"{100 * sum(v) / total:.2f}% |")
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def cmd_traffic_summary(args):
+    """Counter bytes per step (profiles/traffic.json) against the algorithmic bytes and the
+    times of a bench.py run on the same workload."""
+    wl, hdr = _shape_header(args.workload)
+    bench = _bench_line(args.bench)
+    tab = json.load(open(args.traffic))
+    eb = 2 if wl.dtype == "bf16" else 4
+    steps = step_kernels(wl.d, wl.d * eb // 16)
+    out = [f"# HBM traffic: every kernel of the {wl.L // 1024}K op ({hdr}, "
+           f"K_b={bench['budget'][0]})", "",
+           "Commands (from the repository root `$R`, one counter per process):", "", "```",
+           args.command, "```", "",
+           "`profiling.py run --path all` copies 1 GiB device to device (the runtime blit "
+           "`__amd_rocclr_copyBuffer`, the calibration), then runs `tsa_forward`, `tsa_score`, "
+           "`tsa_select`, `tsa_gather` (Q, K and V) and `tsa_scatter` on the workload's own "
+           "seeded inputs. The blit reads FETCH_SIZE = 0.5 GiB and WRITE_SIZE = 1 GiB for 1 GiB "
+           "moved each way, so FETCH_SIZE is scaled by 2 and WRITE_SIZE by 1 "
+           "(`profiles/traffic.json` holds the exact factors and each kernel source's hash; "
+           "`bench.py` reports these bytes only while the hash matches). Times are the per-kernel "
+           f"breakdown of the bench run of {args.bench_label}.", "",
+           "| step | kernels | algorithmic bytes | counter bytes (fetch + write) | counter / "
+           "algorithmic | ms (bench) | GB/s algorithmic | GB/s counters |",
+           "|---|---|---|---|---|---|---|---|"]
+    per_kernel = []
+    for step, kns in steps.items():
+        k = bench["kernels"][step]
+        f = sum(tab[n][wl.name]["fetch_bytes_per_launch"] for n in kns)
+        w = sum(tab[n][wl.name]["write_bytes_per_launch"] for n in kns)
+        alg = k["algorithmic_bytes"]
+        out.append(f"| {step} | {', '.join('`' + n + '`' for n in kns)} | {alg / 1e6:.1f} MB | "
+                   f"{f / 1e6:.1f} + {w / 1e6:.1f} MB | {(f + w) / alg:.2f} | {k['ms']:.4f} | "
+                   f"{alg / (k['ms'] * 1e-3) / 1e9:.0f} | {(f + w) / (k['ms'] * 1e-3) / 1e9:.0f} |")
+    out += ["", "Per kernel (mean per dispatch):", "", "| kernel | source | fetch | write |",
+            "|---|---|---|---|"]
+    for n in sorted(tab):
+        e = tab[n].get(wl.name)
+        if not e or e.get("path") != "all":
+            continue
+        out.append(f"| `{n}` | {e.get('source', 'attention.hip')} | "
+                   f"{e['fetch_bytes_per_launch'] / 1e6:.2f} MB | {e['write_bytes_per_launch'] / 1e6:.2f} MB |")
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def cmd_attention_counters(args):
+    """FETCH/WRITE bytes of the three attention instantiations and the SQ counters of the
+    whole op's attention, with the counted launches' durations."""
+    wl, hdr = _shape_header(args.workload)
+    K = args.budget
+    out = [f"# Counters: attention kernels on the {wl.L // 1024}K workload ({hdr}, K_b={K})", "",
+           "Commands (from the repository root `$R`; one counter pass per process):", "", "```",
+           args.command, "```", "",
+           "`profiling.py run` first copies 1 GiB device to device (the runtime blit kernel "
+           "`__amd_rocclr_copyBuffer`, the calibration), then runs `--path forward`: "
+           "`tsa_forward` on the workload's own seeded inputs; `--path fused`: "
+           "`tsa_forward_fused` on the same inputs; `--path compact`: one `tsa_attention` on "
+           "random bf16 tensors of the compact shape with the headline budget.", "",
+           "## HBM traffic per launch", "",
+           "The blit of 1 GiB reads FETCH_SIZE = 0.5 GiB and WRITE_SIZE = 1 GiB, so FETCH_SIZE is "
+           "scaled by 2 and WRITE_SIZE by 1. The write scale is confirmed by the attention "
+           f"kernels themselves: they write exactly the output rows, {wl.B * wl.Hq} x {K} x "
+           f"{wl.d * 2} B = {wl.B * wl.Hq * K * wl.d * 2 / 1e9:.3f} GB.", "",
+           "| kernel | FETCH_SIZE raw (KiB) | fetch bytes | WRITE_SIZE raw (KiB) | write bytes | "
+           "total | counted launches |", "|---|---|---|---|---|---|---|"]
+    for path in ("forward", "fused", "compact"):
+        kname = f"attn_fwd_bf16<{wl.d}, {KERNEL_ARGS[path]}>"
+        vals = {}
+        for c, d in (("FETCH_SIZE", getattr(args, f"fetch_{path}")),
+                     ("WRITE_SIZE", getattr(args, f"write_{path}"))):
+            rows = list(csv.DictReader(open(_first(d, "*counter_collection.csv"))))
+            copy = max(float(r["Counter_Value"]) for r in rows
+                       if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == c)
+            att = [r for r in rows if short_name(r["Kernel_Name"]) == kname and r["Counter_Name"] == c]
+            raw = sum(float(r["Counter_Value"]) for r in att) / len(att)
+            ms = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in att]
+            vals[c] = (raw, raw * COPY_BYTES / (copy * 1024.0) * 1024.0, COPY_BYTES / (copy * 1024.0), ms)
+        f, w = vals["FETCH_SIZE"], vals["WRITE_SIZE"]
+        out.append(f"| `{kname}` | {f[0]:.0f} | {f[1] / 1e9:.2f} GB (x{f[2]:.4f}) | {w[0]:.0f} | "
+                   f"{w[1] / 1e9:.3f} GB (x{w[2]:.2f}) | {(f[1] + w[1]) / 1e9:.2f} GB | "
+                   f"{', '.join(f'{m:.2f}' for m in f[3] + w[3])} ms |")
+        if path == "forward":
+            fwd = (f[1] + w[1], f[1], sum(f[3] + w[3]) / len(f[3] + w[3]))
+    alg = 4 * wl.B * wl.Hq * K * wl.d * 2
+    flops = 2.0 * wl.d * K * (K + 1) * wl.B * wl.Hq
+    out += ["", f"Algorithmic minimum: Q, K, V read once and O written once = 4 x {wl.B * wl.Hq} x "
+            f"{K} x {wl.d * 2} B = {alg / 1e9:.2f} GB. About {fwd[1] / 1e9:.0f} GB are fetched because "
+            "every workgroup streams all the K/V tiles below its diagonal and part of those re-reads "
+            f"miss the L2. For the whole op's attention, at {fwd[2]:.1f} ms per counted launch that is "
+            f"{fwd[1] / (fwd[2] * 1e-3) / 1e12:.2f} TB/s, {100 * fwd[1] / (fwd[2] * 1e-3) / 8e12:.1f}% "
+            f"of the 8 TB/s HBM bound. The kernel does {flops / fwd[1]:.0f} FLOP per fetched byte "
+            "against a ridge of 312: it is MFMA/issue-bound, not memory-bound.", ""]
+    rows = list(csv.DictReader(open(_first(args.sq, "*counter_collection.csv"))))
+    kname = f"attn_fwd_bf16<{wl.d}, {KERNEL_ARGS['forward']}>"
+    att = [r for r in rows if short_name(r["Kernel_Name"]) == kname]
+    vals = {r["Counter_Name"]: float(r["Counter_Value"]) for r in att}
+    us = (int(att[0]["End_Timestamp"]) - int(att[0]["Start_Timestamp"])) / 1e3
+    cyc = vals["GRBM_GUI_ACTIVE"] / args.xcds
+    busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * args.cus * 4)
+    clk = cyc / (us * 1e-6) / 1e9
+    out += ["## SQ counters (the whole op's attention, one launch)", "",
+            "Counted in the `--path all` run of `profiling.py` (command in "
+            "`kernels_llama8b_L128k_sq.md`, which also lists every other kernel of the op); this "
+            f"counted launch ran {us / 1e3:.2f} ms.", "", "| counter | value |", "|---|---|"]
+    for c in SQ_COUNTERS:
+        out.append(f"| {c} | {vals[c]:.4g} |")
+    mf = vals["SQ_INSTS_MFMA"]
+    out += ["",
+            f"- MFMA pipe busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {args.xcds} XCDs x "
+            f"{args.cus * 4} SIMDs) = {busy:.3f}; SQ_INSTS_MFMA = {mf:.4g} against "
+            f"{flops / 32768:.4g} for the algorithmic FLOPs ({mf * 32768 / flops:.3f}x).",
+            f"- Non-MFMA VALU instructions per MFMA = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / "
+            f"SQ_INSTS_MFMA = {(vals['SQ_INSTS_VALU'] - mf) / mf:.2f}.",
+            f"- Clock: GRBM_GUI_ACTIVE / {args.xcds} = {cyc:.4g} cycles over the counted "
+            f"{us / 1e3:.2f} ms = {clk:.2f} GHz. At that clock the MFMA peak is 2.5 PF x "
+            f"{clk:.2f}/2.4 = {2.5 * clk / 2.4:.2f} PF, and {busy:.3f} busy of it is "
+            f"{busy * 2.5 * clk / 2.4 * 1000:.0f} TFLOP/s."]
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+SQ_COUNTERS = ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+               "SQ_INSTS_LDS", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE"]
+
+
+def cmd_sq_summary(args):
+    """SQ counters of every library kernel of a `run --path all` process."""
+    wl, hdr = _shape_header(args.workload)
+    rows = list(csv.DictReader(open(_first(args.sq, "*counter_collection.csv"))))
+    per = {}
+    for r in rows:
+        n = short_name(r["Kernel_Name"])
+        if kernel_source(n) is None:
+            continue
+        d = per.setdefault(n, {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    simds = args.cus * 4
+    out = [f"# SQ counters: the kernels of the {wl.L // 1024}K op ({hdr})", "",
+           "Command (from the repository root `$R`):", "", "```", args.command, "```", "",
+           f"Means per dispatch. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / "
+           f"{args.xcds} XCDs x {simds} SIMDs). VALU / MFMA counts the non-MFMA VALU "
+           "instructions (SQ_INSTS_VALU includes the MFMAs). For short kernels the counter "
+           "window is longer than the kernel, so their busy figures are lower bounds.", "",
+           "| kernel | dispatch us (counted) | waves | MFMA busy | VALU / MFMA | VALU instr per wave "
+           "| LDS instr per wave |", "|---|---|---|---|---|---|---|"]
+    clock = None
+    for n in sorted(per, key=lambda k: max(d["us"] for d in per[k].values())):
+        ds = list(per[n].values())
+        m = {c: sum(d.get(c, 0.0) for d in ds) / len(ds) for c in SQ_COUNTERS + ["us"]}
+        cyc = m["GRBM_GUI_ACTIVE"] / args.xcds
+        busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * simds) if cyc else 0.0
+        mf = m["SQ_INSTS_MFMA"]
+        ratio = f"{(m['SQ_INSTS_VALU'] - mf) / mf:.2f}" if mf else "no MFMA"
+        w = m["SQ_WAVES"] or 1.0
+        out.append(f"| `{n}` | {m['us']:.1f} | {m['SQ_WAVES']:.0f} | {busy:.3f} | {ratio} | "
+                   f"{m['SQ_INSTS_VALU'] / w:.0f} | {m['SQ_INSTS_LDS'] / w:.0f} |")
+        if n.startswith("attn_fwd"):
+            clock = (n, m["us"], cyc / (m["us"] * 1e-6) / 1e9, busy, ratio)
+    if clock:
+        out += ["", f"The `{clock[0]}` launch counted here ran {clock[1] / 1e3:.2f} ms; "
+                f"GRBM_GUI_ACTIVE / {args.xcds} over it is a clock of {clock[2]:.2f} GHz, so its "
+                f"MFMA pipe was busy {clock[3]:.3f} of the cycles at that clock, with {clock[4]} "
+                "non-MFMA VALU instructions per MFMA."]
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -244,6 +504,41 @@ def main():
     a.add_argument("--workload", default="llama8b_bf16_L128k")
     a.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
     a.set_defaults(fn=cmd_summarize_all)
+    t = sub.add_parser("trace-summary")
+    t.add_argument("--trace", required=True, help="rocprofv3 --kernel-trace --stats output dir")
+    t.add_argument("--bench", required=True, help="the bench.py output of the same run")
+    t.add_argument("--workload", default="llama8b_bf16_L128k")
+    t.add_argument("--command", required=True)
+    t.add_argument("--out", required=True)
+    t.set_defaults(fn=cmd_trace_summary)
+    f = sub.add_parser("traffic-summary")
+    f.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    f.add_argument("--bench", required=True, help="a bench.py output on the same workload")
+    f.add_argument("--bench-label", default="", help="how the summary names that bench run")
+    f.add_argument("--workload", default="llama8b_bf16_L128k")
+    f.add_argument("--command", required=True)
+    f.add_argument("--out", required=True)
+    f.set_defaults(fn=cmd_traffic_summary)
+    c = sub.add_parser("attention-counters")
+    for path in ("forward", "fused", "compact"):
+        c.add_argument(f"--fetch-{path}", required=True)
+        c.add_argument(f"--write-{path}", required=True)
+    c.add_argument("--sq", required=True)
+    c.add_argument("--workload", default="llama8b_bf16_L128k")
+    c.add_argument("--budget", type=int, default=123997)
+    c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--command", required=True)
+    c.add_argument("--out", required=True)
+    c.set_defaults(fn=cmd_attention_counters)
+    q = sub.add_parser("sq-summary")
+    q.add_argument("--sq", required=True, help="rocprofv3 --pmc SQ_* output dir")
+    q.add_argument("--workload", default="llama8b_bf16_L128k")
+    q.add_argument("--cus", type=int, default=256)
+    q.add_argument("--xcds", type=int, default=8)
+    q.add_argument("--command", required=True)
+    q.add_argument("--out", required=True)
+    q.set_defaults(fn=cmd_sq_summary)
     args = ap.parse_args()
     args.fn(args)
 
