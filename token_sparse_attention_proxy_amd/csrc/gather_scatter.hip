@@ -26,12 +26,11 @@ namespace {
 constexpr int kThreads = 256;
 // Rows per block, measured at the 128K shape: the gather of Q, K and V, the
 // scatter and the source-driven K/V gather run best with 32 (the latter 2.4%
-// faster than 64, 4% than 128), the index-driven K/V gather and the zero fill
-// with 128.
+// faster than 64, 4% than 128), the index-driven K/V gather with 128.
 constexpr int kRowsGatherQKV = 32;
 constexpr int kRowsGatherKV = 128;
 constexpr int kRowsScatter = 32;
-constexpr int kRowsZero = 128;
+constexpr int kZeroWaveRows = 256;     // zero fill: rows per wave
 constexpr int kRowsByRank = 32;
 
 // VPR: 16-byte vectors per row (row bytes / 16).  One block copies compact
@@ -135,34 +134,75 @@ __global__ __launch_bounds__(kThreads) void scatter_rows(const u32x4* __restrict
                                                          const int32_t* __restrict__ rank,
                                                          u32x4* __restrict__ o, int L) {
   constexpr int kRowsPerPass = kThreads / VPR;
+  constexpr int kIter = (kRowsScatter + kRowsPerPass - 1) / kRowsPerPass;
   const int bh = blockIdx.y;
   const int j0 = blockIdx.x * kRowsScatter;
   const int sub = threadIdx.x / VPR, vec = threadIdx.x % VPR;
   const int64_t hrow = int64_t(bh) * L;
-  for (int j = j0 + sub; j < min(j0 + kRowsScatter, L); j += kRowsPerPass) {
-    const int r = rank[hrow + j];
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (r >= 0 && r < L) val = oc[(hrow + r) * VPR + vec];
-    __builtin_nontemporal_store(val, o + (hrow + j) * VPR + vec);
+  // rank entries, then the rows they select, then the stores: each phase's
+  // loads overlap instead of every store waiting on its own two loads
+  int r[kIter];
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    const int j = j0 + sub + i * kRowsPerPass;
+    r[i] = (j < L && sub + i * kRowsPerPass < kRowsScatter) ? rank[hrow + j] : -1;
+  }
+  u32x4 val[kIter];
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    val[i] = u32x4{0u, 0u, 0u, 0u};
+    if (r[i] >= 0 && r[i] < L) val[i] = oc[(hrow + r[i]) * VPR + vec];
+  }
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    const int j = j0 + sub + i * kRowsPerPass;
+    if (j < L && sub + i * kRowsPerPass < kRowsScatter)
+      __builtin_nontemporal_store(val[i], o + (hrow + j) * VPR + vec);
   }
 }
 
+// Each wave takes kZeroWaveRows consecutive rows of one head in groups of
+// 64: one coalesced load of the group's rank entries, a ballot of the
+// unselected rows, and zero stores of 64 / VPR such rows per instruction.
+// Most rows are selected, so most groups store nothing.
 template <int VPR>
 __global__ __launch_bounds__(kThreads) void zero_rows(const int32_t* __restrict__ rank,
                                                       u32x4* __restrict__ o, int L) {
-  constexpr int kRowsPerPass = kThreads / VPR;
+  constexpr int kGroups = kZeroWaveRows / 64;
+  constexpr int kRowsPerStore = 64 / VPR;
+  static_assert(kGroups * 64 == kZeroWaveRows && kRowsPerStore * VPR == 64, "zero-fill shape");
   const int bh = blockIdx.y;
-  const int j0 = blockIdx.x * kRowsZero;
-  const int sub = threadIdx.x / VPR, vec = threadIdx.x % VPR;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = lane / VPR, vec = lane % VPR;
   const int64_t hrow = int64_t(bh) * L;
-  for (int j = j0 + sub; j < min(j0 + kRowsZero, L); j += kRowsPerPass) {
-    if (rank[hrow + j] < 0) __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, o + (hrow + j) * VPR + vec);
+  const int jw = (int(blockIdx.x) * (kThreads / 64) + wave) * kZeroWaveRows;
+  int r[kGroups];
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    const int j = jw + 64 * g + lane;
+    r[g] = j < L ? rank[hrow + j] : 0;
+  }
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    uint64_t m = __ballot(r[g] < 0);         // wave-uniform: unselected rows of the group
+    while (m) {
+      int row = -1;                            // this lane's row among the next kRowsPerStore
+#pragma unroll
+      for (int t = 0; t < kRowsPerStore; ++t) {
+        const int bit = m ? __builtin_ctzll(m) : -1;
+        m &= m - 1;
+        if (t == sub) row = bit;
+      }
+      if (row >= 0)
+        __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, o + (hrow + jw + 64 * g + row) * VPR + vec);
+    }
   }
 }
 
 template <int VPR>
 hipError_t zero_vpr(const Shape& sh, const int32_t* rank, void* o, hipStream_t st) {
-  dim3 grid((sh.L + kRowsZero - 1) / kRowsZero, sh.B * sh.Hq);
+  constexpr int rows_per_block = kZeroWaveRows * (kThreads / 64);
+  dim3 grid((sh.L + rows_per_block - 1) / rows_per_block, sh.B * sh.Hq);
   zero_rows<VPR><<<grid, kThreads, 0, st>>>(rank, static_cast<u32x4*>(o), sh.L);
   return hipGetLastError();
 }
