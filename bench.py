@@ -31,6 +31,8 @@ Printed as one JSON line, with:
     tau = 0.01, 0.05, 0.1; B=2 64K with 7 query heads per KV head): ms per
     layer of the op and of the dense attention, speedup, K/L, the share of
     the non-attention kernels and the attention's MFMA fraction;
+  * beside every K/L, the importance mass the top 1% of tokens hold per
+    head (how skewed the scores are, which bounds what tau can prune);
   * per kernel, the HBM bytes that rocprofv3 counters recorded for the same
     kernel source (profiles/traffic.json) beside its algorithmic bytes;
   * provenance: source hashes, GPU, ROCm and torch versions, seeds, and a
@@ -168,6 +170,17 @@ def parity_check():
             "worst_rel_err": float(f"{worst:.3e}"), "ok": bool(ok_sets and worst <= 2e-2)}
 
 
+def top1_mass_share(s) -> dict:
+    """Per (b, h): the importance mass held by the top 1% of tokens (the head's largest
+    ceil(L/100) scores over its total), the skew that bounds what any coverage budget prunes."""
+    import torch
+    L = s.shape[-1]
+    kk = max(1, (L + 99) // 100)
+    share = (torch.topk(s, kk, dim=-1).values.sum(-1) / s.sum(-1)).flatten().cpu().numpy()
+    return {"per_head": [round(float(x), 4) for x in share], "mean": round(float(share.mean()), 4),
+            "min": round(float(share.min()), 4), "max": round(float(share.max()), 4)}
+
+
 def sweep_one(name: str, taus, dev, steps: int):
     """One workload of the sweep: the op (tsa_forward) per tau against the dense attention."""
     import torch
@@ -214,6 +227,7 @@ def sweep_one(name: str, taus, dev, steps: int):
         kl = bud / wl.L
         rec = {"workload": name, "tau": float(tau), "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv,
                "L": wl.L, "w": wl.w, "keep_frac": [round(float(x), 5) for x in kl],
+               "top1pct_mass": top1_mass_share(s),
                "ms_per_layer": round(ms, 4), "dense_ms": round(dense_ms, 4),
                "speedup_vs_dense": round(dense_ms / ms, 4),
                "attention_ms": round(attn_ms, 4),
@@ -450,6 +464,7 @@ def main():
                 per_rep[n].append(ev[i].elapsed_time(ev[i + 1]))
     del evict
     steps_ms = {n: float(np.mean(per_rep[n])) for n in names}
+    top1 = top1_mass_share(s)
     log("[bench] kernels ms: " + ", ".join(f"{n} {steps_ms[n]:.3f}" for n in steps_ms))
 
     # ---- the bf16 MFMA ceiling on this GPU, right after the attention launches: a
@@ -661,6 +676,7 @@ def main():
                    "parallelism": "none"},
         "budget": [int(x) for x in bud],
         "keep_frac": [round(int(x) / wl.L, 5) for x in bud],
+        "top1pct_mass": top1,
         "path": args.path,
         "other_path": {"path": other, "ms_per_step": round(other_ms, 4)},
         "dense_ms": None if dense_ms is None else round(dense_ms, 4),
