@@ -194,16 +194,24 @@ def sweep_one(name: str, taus, dev, steps: int):
     shape = (wl.B, wl.Hq, wl.L, wl.d)
     o = torch.empty(shape, dtype=torch.bfloat16, device=dev)
 
+    # Each repetition timed on its own after a 512 MiB write, so that neither the 256 MiB
+    # Infinity Cache nor the L2 holds this workload's tensors from the previous one; the
+    # median is reported.
+    evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
     def timed(fn, reps):
         fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        for _ in range(reps):
+        ts = []
+        for r in range(reps):
+            evict.fill_(r & 0xff)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
             fn()
-        e1.record(st)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+            e1.record(st)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
 
     prob0 = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, float(taus[0]), "bf16")
     dense_ms = timed(lambda: T.tsa_attention(prob0, qd, kd, vd, None, wl.G, o), max(2, steps // 2))
@@ -239,7 +247,7 @@ def sweep_one(name: str, taus, dev, steps: int):
             f"overhead {rec['overhead_share']:.4f}")
         out.append(rec)
         del ws, budget, idx, s, step_ws, rank, kc, vc
-    del qd, kd, vd, o
+    del qd, kd, vd, o, evict
     torch.cuda.empty_cache()
     return out
 
