@@ -434,6 +434,30 @@ def cmd_attention_counters(args):
     print("\n".join(out))
 
 
+def cmd_counter_table(args):
+    """Every counter of the named kernel from one or more counter runs, with the counted
+    launch's duration, raw and per cycle of the launch (GRBM_GUI_ACTIVE / xcds)."""
+    wl, hdr = _shape_header(args.workload)
+    out = [f"# Counters of `{args.kernel}` on the {wl.L // 1024}K workload ({hdr})", "",
+           "Commands (from the repository root `$R`; one pass per process):", "", "```",
+           args.command, "```", "", args.note, "",
+           "| pass | counter | value | per launch cycle | counted launch ms |",
+           "|---|---|---|---|---|"]
+    for i, d in enumerate(args.dirs):
+        rows = [r for r in csv.DictReader(open(_first(d, "*counter_collection.csv")))
+                if short_name(r["Kernel_Name"]) == args.kernel]
+        if not rows:
+            raise SystemExit(f"no {args.kernel} in {d}")
+        vals = {r["Counter_Name"]: float(r["Counter_Value"]) for r in rows}
+        ms = (int(rows[0]["End_Timestamp"]) - int(rows[0]["Start_Timestamp"])) / 1e6
+        cyc = vals.get("GRBM_GUI_ACTIVE", 0.0) / args.xcds
+        for c in sorted(vals):
+            per = f"{vals[c] / cyc:.4g}" if cyc else "-"
+            out.append(f"| {chr(ord('A') + i)} | {c} | {vals[c]:.4g} | {per} | {ms:.2f} |")
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 SQ_COUNTERS = ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
                "SQ_INSTS_LDS", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE"]
 
@@ -531,6 +555,15 @@ def main():
     c.add_argument("--command", required=True)
     c.add_argument("--out", required=True)
     c.set_defaults(fn=cmd_attention_counters)
+    k = sub.add_parser("counter-table")
+    k.add_argument("--dirs", nargs="+", required=True, help="rocprofv3 --pmc output dirs")
+    k.add_argument("--kernel", required=True, help="short kernel name")
+    k.add_argument("--workload", default="llama8b_bf16_L128k")
+    k.add_argument("--xcds", type=int, default=8)
+    k.add_argument("--note", default="")
+    k.add_argument("--command", required=True)
+    k.add_argument("--out", required=True)
+    k.set_defaults(fn=cmd_counter_table)
     q = sub.add_parser("sq-summary")
     q.add_argument("--sq", required=True, help="rocprofv3 --pmc SQ_* output dir")
     q.add_argument("--workload", default="llama8b_bf16_L128k")
