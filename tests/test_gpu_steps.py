@@ -215,6 +215,13 @@ def test_gather_scatter_bit_exact(case):
     bits = o.view(torch.int16 if dt == "bf16" else torch.int32)
     unsel = torch.from_numpy(rank < 0).cuda()
     assert torch.all(bits[unsel] == 0), "unselected rows must be +0.0 bit patterns"
+    # the zero fill of the whole op: exactly the unselected rows become +0.0, the others
+    # keep their contents (ragged L, every row width the kernel instantiates)
+    oz = torch.full((B, Hq, L, d), 7.0, dtype=qd.dtype, device="cuda")
+    T.tsa_zero_unselected(prob, torch.from_numpy(rank).cuda(), oz)
+    zbits = oz.view(torch.int16 if dt == "bf16" else torch.int32)
+    assert torch.all(zbits[unsel] == 0), "zero fill: unselected rows must be +0.0 bit patterns"
+    assert torch.all(oz[~unsel] == 7.0), "zero fill: selected rows must be left as they were"
 
 
 @pytest.mark.parametrize("case", GATHER_CASES + [("bf16", 2, 14, 2, 3000, 128, 2500)],
