@@ -39,8 +39,10 @@
  *     TSA_ERR_WORKSPACE: ws_bytes below what the *_workspace_bytes query
  *     returns, or a null / misaligned (256 B) workspace.
  *     TSA_ERR_HIP: a launch failed; tsa_last_error() holds the detail.
- *   - Threading: no global mutable state except the thread-local error text;
- *     concurrent calls on different streams with different buffers are safe.
+ *   - Threading: no global mutable state except the thread-local error text
+ *     and the per-device scratch address table of tsa_forward_fused_noalloc
+ *     (filled once per device, under a lock); concurrent calls on different
+ *     streams with different buffers are safe.
  */
 #ifndef TSA_H_
 #define TSA_H_
@@ -95,7 +97,8 @@ typedef struct tsa_problem {
 /* "Budget" below means budget[b] for the main reading and budget[b,h] under
  * TSA_FLAG_PER_HEAD_BUDGET; K_b (or K_bh) is that value. */
 
-/* Human-readable name of a status code (static storage). */
+/* Human-readable name of a status code (static storage); "TSA_ERR_UNKNOWN"
+ * for a value that is not a tsa_status. */
 const char* tsa_status_string(tsa_status st);
 
 /* Detail text of the last failing call on this thread ("" if none). */

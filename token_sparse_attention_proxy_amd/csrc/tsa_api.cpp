@@ -204,7 +204,12 @@ FwdWs fwd_ws_layout(const Shape& s) {
 extern "C" {
 
 const char* tsa_status_string(tsa_status st) {
-  switch (st) {
+  // A C caller may pass any int.  In C++ a value outside the enumerators'
+  // range is undefined once loaded as the enum type, so read the bits as int.
+  static_assert(sizeof(tsa_status) == sizeof(int), "tsa_status is int-sized");
+  int v;
+  std::memcpy(&v, &st, sizeof(v));
+  switch (v) {
     case TSA_OK: return "TSA_OK";
     case TSA_ERR_INVALID_ARG: return "TSA_ERR_INVALID_ARG";
     case TSA_ERR_UNSUPPORTED: return "TSA_ERR_UNSUPPORTED";
