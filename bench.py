@@ -186,6 +186,7 @@ def sweep_one(name: str, taus, dev, steps: int):
     import torch
     from token_sparse_attention_proxy_amd import inputs
     from token_sparse_attention_proxy_amd import tsa as T
+    from token_sparse_attention_proxy_amd._lib import FORWARD_FUSED_MAX_L
     wl = inputs.WORKLOADS[name]
     q, k, v = inputs.make_qkv(wl)
     qd, kd, vd = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v))
@@ -194,60 +195,78 @@ def sweep_one(name: str, taus, dev, steps: int):
     shape = (wl.B, wl.Hq, wl.L, wl.d)
     o = torch.empty(shape, dtype=torch.bfloat16, device=dev)
 
-    # Each repetition timed on its own after a 512 MiB write, so that neither the 256 MiB
-    # Infinity Cache nor the L2 holds this workload's tensors from the previous one; the
-    # median is reported.
+    # Each repetition of each call is timed on its own after a 512 MiB write, so that neither
+    # the 256 MiB Infinity Cache nor the L2 holds this workload's tensors from the previous
+    # one. The calls compared are interleaved, in alternating order from one repetition to
+    # the next, so none of them is favoured by its place in the run; medians are reported.
     evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
-    def timed(fn, reps):
-        fn()
-        torch.cuda.synchronize()
-        ts = []
-        for r in range(reps):
-            evict.fill_(r & 0xff)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(st)
+    def timed(fns: dict, reps):
+        for fn in fns.values():
             fn()
-            e1.record(st)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return float(np.median(ts))
+        torch.cuda.synchronize()
+        ts = {n: [] for n in fns}
+        items = list(fns.items())
+        for r in range(reps):
+            for n, fn in (items if r % 2 == 0 else items[::-1]):
+                evict.fill_(r & 0xff)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                fn()
+                e1.record(st)
+                torch.cuda.synchronize()
+                ts[n].append(e0.elapsed_time(e1))
+        return {n: float(np.median(v)) for n, v in ts.items()}
 
     prob0 = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, float(taus[0]), "bf16")
-    dense_ms = timed(lambda: T.tsa_attention(prob0, qd, kd, vd, None, wl.G, o), max(2, steps // 2))
     dense_tf = attention_flops([wl.L] * wl.B, wl.Hq, wl.d)
+    o2 = torch.empty(shape, dtype=torch.bfloat16, device=dev)
     out = []
     for tau in taus:
         prob = dataclasses.replace(prob0, tau=float(tau))
         ws = torch.empty(T.forward_workspace_bytes(prob), dtype=torch.uint8, device=dev)
         budget = torch.empty((wl.B,), dtype=torch.int32, device=dev)
         idx = torch.empty((wl.B, wl.Hq, wl.L), dtype=torch.int32, device=dev)
-        ms = timed(lambda: T.tsa_forward(prob, qd, kd, vd, o, budget, idx, ws), steps)
+        T.tsa_forward(prob, qd, kd, vd, o, budget, idx, ws)
         bud = budget.cpu().numpy()
-        # the op's attention alone, on the compact K and V the op leaves in its workspace
+        # the op's attention alone needs the compact K and V: its own workspace
         s = torch.empty((wl.B, wl.Hq, wl.L), dtype=torch.float32, device=dev)
         step_ws = torch.empty(T.workspace_bytes(prob), dtype=torch.uint8, device=dev)
         T.tsa_score(prob, qd, kd, s, step_ws)
         _, rank = T.tsa_select(prob, s, budget, None, None, step_ws)
         kc, vc = T.tsa_gather_kv(prob, kd, vd, rank)
-        attn_ms = timed(lambda: T.tsa_attention_qo_indexed(prob, qd, kc, vc, idx, budget, o), steps)
+        # tsa_forward; the same op through the fused path (the attention reads K and V through
+        # the index set instead of compact copies: the same bits, another cost split; up to
+        # 32K tokens tsa_forward runs these kernels itself); the attention tsa_forward runs,
+        # alone; the dense attention on the same tensors
+        if wl.L <= FORWARD_FUSED_MAX_L:
+            attn = lambda: T.tsa_attention_indexed(prob, qd, kd, vd, idx, budget, o2)   # noqa: E731
+        else:
+            attn = lambda: T.tsa_attention_qo_indexed(prob, qd, kc, vc, idx, budget, o2)   # noqa: E731
+        t = timed({"op": lambda: T.tsa_forward(prob, qd, kd, vd, o, budget, idx, ws),
+                   "fused": lambda: T.tsa_forward_fused(prob, qd, kd, vd, o, budget, idx, ws),
+                   "attention": attn,
+                   "dense": lambda: T.tsa_attention(prob0, qd, kd, vd, None, wl.G, o2)}, steps)
+        ms, fused_ms, attn_ms, dense_ms = t["op"], t["fused"], t["attention"], t["dense"]
         fl = attention_flops(bud, wl.Hq, wl.d)
         kl = bud / wl.L
         rec = {"workload": name, "tau": float(tau), "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv,
                "L": wl.L, "w": wl.w, "keep_frac": [round(float(x), 5) for x in kl],
                "top1pct_mass": top1_mass_share(s),
-               "ms_per_layer": round(ms, 4), "dense_ms": round(dense_ms, 4),
+               "ms_per_layer": round(ms, 4), "fused_ms_per_layer": round(fused_ms, 4),
+               "dense_ms": round(dense_ms, 4),
                "speedup_vs_dense": round(dense_ms / ms, 4),
                "attention_ms": round(attn_ms, 4),
                "overhead_share": round((ms - attn_ms) / attn_ms, 4),
                "attention_mfma_frac": round(fl / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                "dense_mfma_frac": round(dense_tf / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        log(f"[bench] sweep {name} tau={tau}: {ms:.3f} ms vs dense {dense_ms:.3f} ms "
+        log(f"[bench] sweep {name} tau={tau}: {ms:.3f} ms (fused path {fused_ms:.3f}) vs dense "
+            f"{dense_ms:.3f} ms "
             f"(x{dense_ms / ms:.3f}), K/L {kl.round(4)}, attention {attn_ms:.3f} ms, "
             f"overhead {rec['overhead_share']:.4f}")
         out.append(rec)
         del ws, budget, idx, s, step_ws, rank, kc, vc
-    del qd, kd, vd, o, evict
+    del qd, kd, vd, o, o2, evict
     torch.cuda.empty_cache()
     return out
 

@@ -211,10 +211,12 @@ tsa_status tsa_scatter(const tsa_problem* prob, const void* oc, const int32_t* r
 /* The whole op: score -> budget -> select -> gather -> attention -> scatter,
  * run as tsa_score -> tsa_budget -> tsa_select -> tsa_gather of K and V ->
  * tsa_zero_unselected -> tsa_attention_qo_indexed, which gives the same bits
- * without materialising the compact Q and O.  o: [B,Hq,L,d] output
- * (unselected rows exactly zero); budget: [B] int32 output; idx: [B,Hq,L]
- * int32 output (as tsa_select).  ws must hold tsa_forward_workspace_bytes(prob)
- * bytes. */
+ * without materialising the compact Q and O.  For L <= 32768 it runs the
+ * kernels of tsa_forward_fused instead (the attention reads K and V through
+ * the index set, faster at those lengths), with the same bits again.
+ * o: [B,Hq,L,d] output (unselected rows exactly zero); budget: [B] int32
+ * output; idx: [B,Hq,L] int32 output (as tsa_select).  ws must hold
+ * tsa_forward_workspace_bytes(prob) bytes. */
 tsa_status tsa_forward(const tsa_problem* prob, const void* q, const void* k, const void* v,
                        void* o, int32_t* budget, int32_t* idx, void* ws, size_t ws_bytes,
                        void* stream);

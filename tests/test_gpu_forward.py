@@ -84,6 +84,29 @@ def test_steps_compose_to_forward():
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
 
 
+def test_compact_kv_steps_compose_to_forward():
+    """The long-context composition of the whole op (K/V-only gather through the rank map, zero
+    fill, attention with Q read and O written through the index set), called one by one at a
+    small ragged size, gives tsa_forward's result bit for bit; tsa_forward itself takes the
+    fused kernels at this length, so both compositions are held to the same bits."""
+    wl = SMALL[1]
+    say("case compact K/V steps == forward")
+    q, k, v = inputs.make_qkv(wl)
+    prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, 0.2, wl.dtype)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    o, budget, idx = T.tsa_forward(prob, qd, kd, vd)
+    s = T.tsa_score(prob, qd, kd)
+    bud = T.tsa_budget(prob, s)
+    idx2, rank = T.tsa_select(prob, s, bud)
+    kc, vc = T.tsa_gather_kv(prob, kd, vd, rank)
+    o2 = torch.full_like(qd, float("nan"))
+    T.tsa_zero_unselected(prob, rank, o2)
+    T.tsa_attention_qo_indexed(prob, qd, kc, vc, idx2, bud, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(budget, bud) and torch.equal(idx, idx2)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+
+
 # ---------------------------------------------------------------- full sizes
 FULL = ["tiny_mha_f32_L1k", "llama8b_bf16_L8k", "llama8b_bf16_L32k_zipf", "llama8b_bf16_L128k",
         "gqa7_bf16_B2_L64k"]

@@ -61,6 +61,7 @@ _SIGNATURES = {
 }
 
 NOALLOC_SCRATCH_BYTES = 128 << 20    # TSA_NOALLOC_SCRATCH_BYTES in include/tsa.h
+FORWARD_FUSED_MAX_L = 32768          # tsa_forward runs the fused kernels up to this L (include/tsa.h)
 
 _lib = None
 

@@ -20,12 +20,14 @@
 //      exceeds thr (the same integer scan everywhere), and copies that
 //      bucket's values into a candidate list (order free: only the multiset
 //      matters below);
-//   3. cut (one workgroup per budget row): every value below the bucket is
-//      pruned; inside it, a most-significant-digit radix descent over the
-//      candidates (in LDS when they fit) moves into the first digit bucket
-//      whose running mass exceeds what is left of thr, and stops when that
-//      bucket holds one value or all bits are fixed; all values left are
-//      then equal and P follows in closed form.
+//   3. cut, in the same launch, by the last workgroup of each budget row to
+//      finish its extraction (a counter taken after a device-scope fence
+//      tells it that every candidate is written; no workgroup waits): every
+//      value below the bucket is pruned; inside it, a most-significant-digit
+//      radix descent over the candidates (in LDS when they fit) moves into
+//      the first digit bucket whose running mass exceeds what is left of
+//      thr, and stops when that bucket holds one value or all bits are
+//      fixed; all values left are then equal and P follows in closed form.
 //
 // Alternative readings: with per-head budgets each (b, h) is a row of its
 // own (sigma = that head's quantised scores, thr = floor(tau*2^50)); with a
@@ -37,17 +39,20 @@
 namespace tsa {
 namespace {
 
-constexpr int kThreads = 256;                // sigma and extract passes
+constexpr int kThreads = 256;                // sigma pass
 constexpr int kPer = 4;                      // sigma pass: tokens per thread (one 16-byte load per head)
 constexpr int kSigChunk = kThreads * kPer;   // tokens per sigma workgroup
-constexpr int kExPer = 8;                    // extract pass: tokens per thread
-constexpr int kExChunk = kThreads * kExPer;  // tokens per extract workgroup
+constexpr int kCutThreads = 1024;            // extract and cut
+constexpr int kExPer = 2;                    // extract pass: tokens per thread (one 16-byte load)
+constexpr int kExChunk = kCutThreads * kExPer;   // tokens per extract workgroup
 constexpr int kLogBuckets = kBudgetLogBuckets;   // 4096: 6 bits of bit length, 6 after the leading one
-constexpr int kLogPerThread = kLogBuckets / kThreads;
-constexpr int kCutThreads = 1024;
 constexpr int kDigitBits = 11;
 constexpr int kBuckets = 1 << kDigitBits;
 constexpr int kCandLds = 12288;              // candidates held in LDS by the cut (96 KiB)
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt 0 only (expcnt 7
+// and lgkmcnt 15 do not wait): every vector memory operation of the wave,
+// stores included, has completed.
+constexpr int kWaitVmem = 0x0f70;
 
 __device__ __forceinline__ uint64_t quantise(float x) {
   // fmaxf/fminf return the non-NaN operand, so NaN counts as 0.
@@ -134,9 +139,11 @@ struct Cross {
   uint64_t mass_below, cnt_below;
   int bucket, crossed;
 };
+template <int NT>
 __device__ __forceinline__ Cross find_cross(const uint32_t* __restrict__ hc,
                                             const uint64_t* __restrict__ hm, uint64_t thr,
                                             uint64_t* tmp, uint64_t* sh) {
+  constexpr int kLogPerThread = kLogBuckets / NT;
   const int t = threadIdx.x;
   const int d0 = kLogPerThread * t;              // this thread's buckets, ascending
   uint64_t m[kLogPerThread];
@@ -181,84 +188,93 @@ __device__ __forceinline__ Cross find_cross(const uint32_t* __restrict__ hc,
   return c;
 }
 
-// The values of the crossing bucket, appended to cand[r] (ncand[r] counts
-// them; one atomic per workgroup reserves its slots).  Workgroup (0, r) also
-// records the crossing: state[r] = (bucket, mass below, count below, crossed).
-__global__ __launch_bounds__(kThreads) void budget_extract(
+// The values of the crossing bucket, appended to cand[r] by every workgroup
+// of row r (ncand[r] counts them; one atomic per workgroup reserves its
+// slots), then the exact cut inside the bucket by the last workgroup of the
+// row to finish: done[r] counts finished workgroups.  Each workgroup's
+// candidate stores are made visible device-wide before its count (release),
+// and the last workgroup's reads come after its count (acquire), so it sees
+// every candidate.  No workgroup waits for another.
+__global__ __launch_bounds__(kCutThreads) void budget_extract_cut(
     const uint64_t* __restrict__ sigma, const uint32_t* __restrict__ hcnt,
-    const uint64_t* __restrict__ hmass, uint64_t* __restrict__ cand, uint32_t* __restrict__ ncand,
-    uint64_t* __restrict__ state, int L, int nc, uint64_t thr) {
-  __shared__ uint64_t tmp[17];
-  __shared__ uint64_t sh[3];
-  __shared__ uint32_t base_s;
-  const int r = blockIdx.y;
-  const int t = threadIdx.x;
-  const Cross c = find_cross(hcnt + int64_t(r) * kLogBuckets, hmass + int64_t(r) * kLogBuckets, thr,
-                             tmp, sh);
-  if (blockIdx.x == 0 && t == 0) {
-    state[int64_t(r) * 4 + 0] = uint64_t(c.bucket);
-    state[int64_t(r) * 4 + 1] = c.mass_below;
-    state[int64_t(r) * 4 + 2] = c.cnt_below;
-    state[int64_t(r) * 4 + 3] = uint64_t(c.crossed);
-  }
-  if (!c.crossed) return;                          // whole workgroup
-  const int j0 = int(blockIdx.x) * kExChunk + kExPer * t;
-  const uint64_t* sg = sigma + int64_t(r) * L;
-  uint64_t v[kExPer];
-  uint32_t nhit = 0;
-#pragma unroll
-  for (int q = 0; q < kExPer; ++q) {
-    const int j = j0 + q;
-    v[q] = j < nc ? sg[j] : 0;
-    const bool hit = j < nc && log_bucket(v[q]) == c.bucket;
-    nhit += hit;
-    if (!hit) v[q] = ~uint64_t(0);               // marks a miss (no sigma reaches 2^64 - 1)
-  }
-  uint64_t total;
-  const uint64_t off = block_excl_scan_u64(nhit, tmp, &total);
-  if (total == 0) return;                          // whole workgroup
-  if (t == 0) base_s = atomicAdd(&ncand[r], uint32_t(total));
-  __syncthreads();
-  uint64_t* cr = cand + int64_t(r) * L + base_s + off;
-  uint32_t k = 0;
-#pragma unroll
-  for (int q = 0; q < kExPer; ++q)
-    if (v[q] != ~uint64_t(0)) cr[k++] = v[q];
-}
-
-// One workgroup per budget row: the exact cut inside the crossing bucket.
-__global__ __launch_bounds__(kCutThreads) void budget_cut(const uint64_t* __restrict__ cand_g,
-                                                          const uint32_t* __restrict__ ncand,
-                                                          const uint64_t* __restrict__ state,
-                                                          int32_t* __restrict__ budget, int L,
-                                                          int pmax, uint64_t thr) {
+    const uint64_t* __restrict__ hmass, uint64_t* __restrict__ cand_g,
+    uint32_t* __restrict__ ncand, uint32_t* __restrict__ done, int32_t* __restrict__ budget,
+    int L, int nc, int pmax, uint64_t thr) {
   __shared__ uint64_t cand_s[kCandLds];
   __shared__ uint32_t cnt[kBuckets];
   __shared__ uint64_t mass[kBuckets];
   __shared__ uint64_t scan_tmp[17];
+  __shared__ uint64_t sh[3];
+  __shared__ uint32_t base_s;
+  __shared__ int last_s;
   __shared__ int first_cross;
   __shared__ uint64_t sh_below_mass, sh_bucket_mass;
   __shared__ uint32_t sh_below_cnt, sh_bucket_cnt;
 
-  const int r = blockIdx.x;
+  const int r = blockIdx.y;
   const int t = threadIdx.x;
-  const int bucket = int(state[int64_t(r) * 4 + 0]);
-  const uint64_t mass_out = state[int64_t(r) * 4 + 1];   // pruned: every value below the bucket
-  const uint64_t cnt_out = state[int64_t(r) * 4 + 2];
-  const bool crossed = state[int64_t(r) * 4 + 3] != 0;
-  if (!crossed) {                       // the whole candidate mass stays within thr
+  const int j0 = int(blockIdx.x) * kExChunk + kExPer * t;
+  const uint64_t* sg = sigma + int64_t(r) * L;
+  uint64_t v[kExPer];
+#pragma unroll
+  for (int q = 0; q < kExPer; ++q) v[q] = j0 + q < nc ? sg[j0 + q] : 0;   // in flight during the scan
+  const Cross c = find_cross<kCutThreads>(hcnt + int64_t(r) * kLogBuckets,
+                                          hmass + int64_t(r) * kLogBuckets, thr, scan_tmp, sh);
+  uint64_t* cand_row = cand_g + int64_t(r) * L;
+  if (c.crossed) {                                 // uniform over the workgroup
+    uint32_t nhit = 0;
+#pragma unroll
+    for (int q = 0; q < kExPer; ++q) {
+      const int j = j0 + q;
+      const bool hit = j < nc && log_bucket(v[q]) == c.bucket;
+      nhit += hit;
+      if (!hit) v[q] = ~uint64_t(0);             // marks a miss (no sigma reaches 2^64 - 1)
+    }
+    uint64_t total;
+    const uint64_t off = block_excl_scan_u64(nhit, scan_tmp, &total);
+    if (total > 0) {                               // uniform
+      if (t == 0) base_s = atomicAdd(&ncand[r], uint32_t(total));
+      __syncthreads();
+      uint64_t* cr = cand_row + base_s + off;
+      uint32_t k = 0;
+#pragma unroll
+      for (int q = 0; q < kExPer; ++q)
+        if (v[q] != ~uint64_t(0)) cr[k++] = v[q];
+    }
+  }
+  // Every wave waits until its candidate stores have reached the L2; after
+  // the barrier, thread 0's release increment writes the L2 back before the
+  // count is taken, so every candidate of the workgroup is visible device-wide
+  // by then.  The workgroup that takes the last count invalidates its caches
+  // (acquire) before reading: one write-back per workgroup, one invalidation
+  // per row.
+  __builtin_amdgcn_s_waitcnt(kWaitVmem);
+  __syncthreads();
+  if (t == 0) {
+    const uint32_t old =
+        __hip_atomic_fetch_add(&done[r], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == gridDim.x - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    last_s = last;
+  }
+  __syncthreads();
+  if (!last_s) return;                   // whole workgroup
+
+  if (!c.crossed) {                      // the whole candidate mass stays within thr
     if (t == 0) budget[r] = L - pmax;
     return;
   }
-  const int n = int(ncand[r]);
-  const uint64_t* cand = cand_g + int64_t(r) * L;
+  const uint64_t mass_out = c.mass_below;   // pruned: every value below the bucket
+  const uint64_t cnt_out = c.cnt_below;
+  const int n = int(__hip_atomic_load(&ncand[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const uint64_t* cand = cand_row;
   if (n <= kCandLds) {
     for (int i = t; i < n; i += kCutThreads) cand_s[i] = cand[i];
     cand = cand_s;                      // generic pointer to LDS from here on
   }
   __syncthreads();
   // Every candidate shares the bit length e and the top seven bits.
-  const int e = bucket >> 6;
+  const int e = c.bucket >> 6;
   int lo = e > 7 ? e - 7 : 0;           // bits below the shared prefix
   const uint64_t room = thr - mass_out;
   uint64_t prefix = n > 0 ? (cand[0] >> lo) : 0;
@@ -332,8 +348,14 @@ __global__ void budget_fill(int32_t* __restrict__ budget, int rows, int L) {
 
 }  // namespace
 
+int64_t budget_clear_words(const Shape& sh) {
+  const StepWs lay = step_ws_layout(sh);
+  return int64_t(lay.bud_ncand + sizeof(uint32_t) * 2 * size_t(sh.bud_rows()) - lay.bud_hcnt) /
+         int64_t(sizeof(uint32_t));
+}
+
 hipError_t launch_budget(const Shape& sh, const float* scores, int32_t* budget, char* ws,
-                         hipStream_t st) {
+                         hipStream_t st, bool cleared) {
   const int rows = sh.bud_rows();
   if (sh.tau == 0.0f) {   // tau = 0 prunes nothing
     budget_fill<<<(rows + 255) / 256, 256, 0, st>>>(budget, rows, sh.L);
@@ -345,7 +367,7 @@ hipError_t launch_budget(const Shape& sh, const float* scores, int32_t* budget, 
   uint32_t* hcnt = reinterpret_cast<uint32_t*>(ws + lay.bud_hcnt);
   uint64_t* hmass = reinterpret_cast<uint64_t*>(ws + lay.bud_hmass);
   uint32_t* ncand = reinterpret_cast<uint32_t*>(ws + lay.bud_ncand);
-  uint64_t* state = reinterpret_cast<uint64_t*>(ws + lay.bud_state);
+  uint32_t* done = ncand + rows;
   const int hpr = sh.per_head() ? 1 : sh.Hq;     // query heads per budget row
   const int nc = sh.L - sh.keep();                // pruning candidates
   const int pmax = nc < sh.L - 1 ? nc : sh.L - 1;
@@ -353,14 +375,16 @@ hipError_t launch_budget(const Shape& sh, const float* scores, int32_t* budget, 
   // the product is exact in double.
   const double x = double(hpr) * double(sh.tau) * 1125899906842624.0;
   const uint64_t thr = uint64_t(x);
-  // the count and mass histograms and the candidate counters are contiguous words
-  const int64_t words = (lay.bud_ncand + sizeof(uint32_t) * rows - lay.bud_hcnt) / sizeof(uint32_t);
-  clear_words<<<unsigned((words + 255) / 256), 256, 0, st>>>(hcnt, words);
+  if (!cleared) {
+    // the count and mass histograms, the candidate and the finished-workgroup
+    // counters are contiguous words
+    const int64_t words = budget_clear_words(sh);
+    clear_words<<<unsigned((words + 255) / 256), 256, 0, st>>>(hcnt, words);
+  }
   budget_sigma<<<dim3((max(nc, 1) + kSigChunk - 1) / kSigChunk, rows), kThreads, 0, st>>>(
       scores, sigma, hcnt, hmass, hpr, sh.L, nc);
-  budget_extract<<<dim3((max(nc, 1) + kExChunk - 1) / kExChunk, rows), kThreads, 0, st>>>(
-      sigma, hcnt, hmass, cand, ncand, state, sh.L, nc, thr);
-  budget_cut<<<rows, kCutThreads, 0, st>>>(cand, ncand, state, budget, sh.L, pmax, thr);
+  budget_extract_cut<<<dim3((max(nc, 1) + kExChunk - 1) / kExChunk, rows), kCutThreads, 0, st>>>(
+      sigma, hcnt, hmass, cand, ncand, done, budget, sh.L, nc, pmax, thr);
   return hipGetLastError();
 }
 

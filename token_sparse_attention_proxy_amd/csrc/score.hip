@@ -121,11 +121,22 @@ __global__ __launch_bounds__(kThreads) void score_pass1(const T* __restrict__ q,
 // One wave per proxy row: combine the chunk partials.  Lane i takes chunks
 // i, i+64, ...; the row max is a wave max, the sum is accumulated in fp64 per
 // lane and then reduced over the lanes in a fixed butterfly order, so the
-// result is deterministic.
+// result is deterministic.  The grid also zeroes the words of two ranges
+// (n0, n1 may be 0): in the whole op, the counters that the budget and the
+// selection start from.
 constexpr int kMergeWaves = 4;
 __global__ __launch_bounds__(64 * kMergeWaves) void score_merge(const float2* __restrict__ part,
                                                                 float2* __restrict__ rowstat,
-                                                                int64_t rows, int n_chunk) {
+                                                                int64_t rows, int n_chunk,
+                                                                uint32_t* __restrict__ z0,
+                                                                int64_t n0,
+                                                                uint32_t* __restrict__ z1,
+                                                                int64_t n1) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n0 + n1; i += stride) {
+    if (i < n0) z0[i] = 0u;
+    else z1[i - n0] = 0u;
+  }
   const int64_t r = int64_t(blockIdx.x) * kMergeWaves + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= rows) return;                   // whole wave exits together
@@ -454,7 +465,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) 
 
 template <typename T, int D>
 hipError_t run(const Shape& sh, const void* q, const void* k, float* scores, char* ws,
-               hipStream_t st) {
+               hipStream_t st, const StepClear& z) {
   const StepWs lay = step_ws_layout(sh);
   float2* part = reinterpret_cast<float2*>(ws + lay.part);
   float2* rowstat = reinterpret_cast<float2*>(ws + lay.rowstat);
@@ -473,7 +484,7 @@ hipError_t run(const Shape& sh, const void* q, const void* k, float* scores, cha
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), part, sh.Hq, sh.Hkv,
         sh.L, sh.w, nc, cpg, hpg, c, int(sh.causal_proxy()));
     score_merge<<<unsigned((rows + kMergeWaves - 1) / kMergeWaves), 64 * kMergeWaves, 0, st>>>(
-        part, rowstat, rows, nc);
+        part, rowstat, rows, nc, z.p0, z.n0, z.p1, z.n1);
     score_mfma_colsum<D><<<grid, kMThreads, colsum_bytes, st>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), rowstat, scores, sh.Hq,
         sh.Hkv, sh.L, sh.w, nc, cpg, hpg, c, int(sh.causal_proxy()));
@@ -483,7 +494,7 @@ hipError_t run(const Shape& sh, const void* q, const void* k, float* scores, cha
                                                  part, sh.Hq, sh.Hkv, sh.L, sh.w, nc, c,
                                                  int(sh.causal_proxy()));
     score_merge<<<unsigned((rows + kMergeWaves - 1) / kMergeWaves), 64 * kMergeWaves, 0, st>>>(
-        part, rowstat, rows, nc);
+        part, rowstat, rows, nc, z.p0, z.n0, z.p1, z.n1);
     score_pass2<T, D><<<grid, kThreads, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
                                                  rowstat, scores, sh.Hq, sh.Hkv, sh.L, sh.w, c,
                                                  int(sh.causal_proxy()));
@@ -494,12 +505,13 @@ hipError_t run(const Shape& sh, const void* q, const void* k, float* scores, cha
 }  // namespace
 
 hipError_t launch_score(const Shape& sh, const void* q, const void* k, float* scores, char* ws,
-                        hipStream_t st) {
+                        hipStream_t st, const StepClear* clear) {
+  const StepClear z = clear ? *clear : StepClear{nullptr, 0, nullptr, 0};
   if (sh.dtype == TSA_BF16)
-    return sh.d == 128 ? run<uint16_t, 128>(sh, q, k, scores, ws, st)
-                       : run<uint16_t, 64>(sh, q, k, scores, ws, st);
-  return sh.d == 128 ? run<float, 128>(sh, q, k, scores, ws, st)
-                     : run<float, 64>(sh, q, k, scores, ws, st);
+    return sh.d == 128 ? run<uint16_t, 128>(sh, q, k, scores, ws, st, z)
+                       : run<uint16_t, 64>(sh, q, k, scores, ws, st, z);
+  return sh.d == 128 ? run<float, 128>(sh, q, k, scores, ws, st, z)
+                     : run<float, 64>(sh, q, k, scores, ws, st, z);
 }
 
 }  // namespace tsa

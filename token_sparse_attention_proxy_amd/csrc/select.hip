@@ -15,9 +15,13 @@
 //      atomics; every workgroup of the next pass reads that histogram and
 //      picks the digit itself (the same integer scan in every workgroup), so
 //      no pass waits on another inside a launch;
-//   2. a count pass records, per chunk, c_gt = #{key > T} and c_eq =
-//      #{key == T};
-//   3. the compaction pass: with need = K - #{key > T}, token j is kept when
+//   2. the last histogram pass also records, per chunk, the number of keys
+//      above the 22-bit prefix and the suffix sums S[b] = #{keys on the
+//      prefix with last digit >= b}, so that once the last digit d is known
+//      (T = prefix:d) the chunk holds #{key > T} = above + S[d+1] and
+//      #{key == T} = S[d] - S[d+1] keys;
+//   3. the compaction pass picks d itself (the same scan in every
+//      workgroup); with need = K - #{key > T}, token j is kept when
 //      key_j > T, or key_j == T and fewer than `need` T-valued tokens precede
 //      it.  A workgroup starts from the counts of the chunks before it and
 //      runs a block scan per 1024 tokens of packed (greater, equal) counts,
@@ -42,6 +46,8 @@ constexpr int kDigitsPerThread = kBuckets / kThreads;
 constexpr int kWidth[3] = {11, 11, 10};
 constexpr int kLo[3] = {21, 10, 0};             // lowest key bit of each level's digit
 constexpr int kTargetBlocks = 1024;             // workgroups per pass the chunking aims at
+constexpr int kLastBins = 1 << kWidth[2];       // digits of the last level
+static_assert(kSelectTabStride == kLastBins + 2, "per-chunk table: S[0..1024] and the count above");
 
 __device__ __forceinline__ uint32_t score_key(float x) {
   return (x > 0.0f) ? __float_as_uint(x) : 0u;   // NaN, -0, negatives -> 0
@@ -132,13 +138,18 @@ __global__ void sel_clear(uint32_t* __restrict__ p, int64_t n) {
 
 // One histogram level.  hist: [3][heads][kBuckets]; state: [3][heads][2]
 // holds (prefix, above) after the pick of each level.
+// The last level also writes the chunk's table for the compaction:
+// tab[(head * nch + chunk) * kSelectTabStride + b] = S[b] for b <= 1024
+// (S[1024] = 0), and entry 1025 = #{keys whose 22-bit prefix is above the
+// picked one}.
 template <int LEVEL>
 __global__ __launch_bounds__(kThreads) void sel_level(const float* __restrict__ s,
                                                       const int32_t* __restrict__ budget,
                                                       uint32_t* __restrict__ hist,
-                                                      uint32_t* __restrict__ state, int heads,
+                                                      uint32_t* __restrict__ state,
+                                                      uint32_t* __restrict__ tab, int heads,
                                                       int Hq, int L, int bud_b, int bud_h,
-                                                      int keep, int chunk) {
+                                                      int keep, int chunk, int nch) {
   __shared__ uint32_t lh[kBuckets];
   __shared__ uint64_t tmp[17];
   __shared__ int sel[2];
@@ -173,13 +184,15 @@ __global__ __launch_bounds__(kThreads) void sel_level(const float* __restrict__ 
   constexpr int lo = kLo[LEVEL], hi = lo + kWidth[LEVEL];
   for (int i = t; i < kBuckets; i += kThreads) lh[i] = 0u;
   __syncthreads();
+  uint32_t nabove = 0;                              // last level: keys above the prefix
   for (int base = hd.j0; base < hd.j1; base += kStep) {
     load_keys(hd.s, base + kStep + kPer * t, hd.j1, hd.vec, un);
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const uint32_t top = hi >= 32 ? 0u : (u[q] >> hi);
-      if (base + kPer * t + q < hd.j1 && top == prefix)
-        atomicAdd(&lh[(u[q] >> lo) & ((1u << kWidth[LEVEL]) - 1u)], 1u);
+      const bool in = base + kPer * t + q < hd.j1;
+      if (in && top == prefix) atomicAdd(&lh[(u[q] >> lo) & ((1u << kWidth[LEVEL]) - 1u)], 1u);
+      if constexpr (LEVEL == 2) nabove += in && top > prefix;
     }
 #pragma unroll
     for (int q = 0; q < kPer; ++q) u[q] = un[q];
@@ -188,81 +201,85 @@ __global__ __launch_bounds__(kThreads) void sel_level(const float* __restrict__ 
   uint32_t* gh = hist + (int64_t(LEVEL) * heads + hd.bh) * kBuckets;
   for (int i = t; i < kBuckets; i += kThreads)
     if (lh[i]) atomicAdd(&gh[i], lh[i]);
-}
-
-// Picks the last digit (so T is known), stores (T, above) as state level 2,
-// and counts each chunk's tokens above and equal to T: cnt [heads][nch][2].
-__global__ __launch_bounds__(kThreads) void sel_count(const float* __restrict__ s,
-                                                      const int32_t* __restrict__ budget,
-                                                      const uint32_t* __restrict__ hist,
-                                                      uint32_t* __restrict__ state,
-                                                      uint32_t* __restrict__ cnt, int heads,
-                                                      int Hq, int L, int bud_b, int bud_h,
-                                                      int keep, int chunk, int nch) {
-  __shared__ uint64_t tmp[17];
-  __shared__ int sel[2];
-  const Head hd = head_of(s, budget, Hq, L, bud_b, bud_h, keep, chunk);
-  const int t = threadIdx.x;
-  uint32_t u[kPer], un[kPer];
-  load_keys(hd.s, hd.j0 + kPer * t, hd.j1, hd.vec, u);   // in flight during the pick
-  uint32_t prefix = state[(int64_t(1) * heads + hd.bh) * 2];
-  uint32_t above = state[(int64_t(1) * heads + hd.bh) * 2 + 1];
-  uint32_t d;
-  pick_digit(hist + (int64_t(2) * heads + hd.bh) * kBuckets, uint32_t(hd.Kc), d, above, tmp, sel);
-  const uint32_t T = (prefix << kWidth[2]) | d;
-  if (blockIdx.x == 0 && t == 0) {
-    state[(int64_t(2) * heads + hd.bh) * 2] = T;
-    state[(int64_t(2) * heads + hd.bh) * 2 + 1] = above;
-  }
-  uint32_t ngt = 0, neq = 0;
-  for (int base = hd.j0; base < hd.j1; base += kStep) {
-    load_keys(hd.s, base + kStep + kPer * t, hd.j1, hd.vec, un);
+  if constexpr (LEVEL == 2) {
+    // suffix sums of the chunk's last-digit histogram: thread t owns digits
+    // 4t .. 4t + 3; S[b] = (keys on the prefix) - (those with digit < b)
+    static_assert(kLastBins == kThreads * 4, "four digits per thread");
+    uint32_t c[4];
+    uint32_t mine = 0;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const bool in = base + kPer * t + q < hd.j1;
-      ngt += in && u[q] > T;
-      neq += in && u[q] == T;
+    for (int i = 0; i < 4; ++i) {
+      c[i] = lh[4 * t + i];
+      mine += c[i];
     }
+    uint64_t tot;
+    const uint64_t ex = block_excl_scan_u64((uint64_t(nabove) << 32) | mine, tmp, &tot);
+    const uint32_t on_prefix = uint32_t(tot & 0xffffffffu);
+    uint32_t below = uint32_t(ex & 0xffffffffu);
+    uint32_t* tb = tab + (int64_t(hd.bh) * nch + blockIdx.x) * kSelectTabStride;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) u[q] = un[q];
-  }
-  uint64_t tot;
-  block_excl_scan_u64((uint64_t(ngt) << 32) | neq, tmp, &tot);
-  if (t == 0 && int(blockIdx.x) < nch) {
-    cnt[(int64_t(hd.bh) * nch + blockIdx.x) * 2] = uint32_t(tot >> 32);
-    cnt[(int64_t(hd.bh) * nch + blockIdx.x) * 2 + 1] = uint32_t(tot & 0xffffffffu);
+    for (int i = 0; i < 4; ++i) {
+      tb[4 * t + i] = on_prefix - below;
+      below += c[i];
+    }
+    if (t == 0) {
+      tb[kLastBins] = 0u;
+      tb[kLastBins + 1] = uint32_t(tot >> 32);
+    }
   }
 }
 
-// Ascending compaction of each chunk, then the kept window and the -1 fill,
-// split over the workgroups by position.  Grid x covers ceil(L / chunk).
+// Picks the last digit (so T is known), then the ascending compaction of
+// each chunk, then the kept window and the -1 fill, split over the
+// workgroups by position.  Grid x covers ceil(L / chunk).
 __global__ __launch_bounds__(kThreads) void sel_compact(const float* __restrict__ s,
                                                         const int32_t* __restrict__ budget,
+                                                        const uint32_t* __restrict__ hist,
                                                         const uint32_t* __restrict__ state,
-                                                        const uint32_t* __restrict__ cnt,
+                                                        const uint32_t* __restrict__ tab,
                                                         int32_t* __restrict__ idx,
                                                         int32_t* __restrict__ rank, int heads,
                                                         int Hq, int L, int bud_b, int bud_h,
                                                         int keep, int chunk, int nch) {
   __shared__ uint64_t tmp[17];
+  __shared__ int sel[2];
   const Head hd = head_of(s, budget, Hq, L, bud_b, bud_h, keep, chunk);
   const int t = threadIdx.x;
   int32_t* ih = idx + int64_t(hd.bh) * L;
   int32_t* rh = rank + int64_t(hd.bh) * L;
   if (hd.j0 < hd.j1) {
     uint32_t u[kPer], un[kPer];
-    load_keys(hd.s, hd.j0 + kPer * t, hd.j1, hd.vec, u);   // in flight during the carry sums
-    const uint32_t T = state[(int64_t(2) * heads + hd.bh) * 2];
-    const uint32_t above = state[(int64_t(2) * heads + hd.bh) * 2 + 1];
+    load_keys(hd.s, hd.j0 + kPer * t, hd.j1, hd.vec, u);   // in flight during the pick
+    const uint32_t prefix = state[(int64_t(1) * heads + hd.bh) * 2];
+    uint32_t above = state[(int64_t(1) * heads + hd.bh) * 2 + 1];
+    uint32_t d;
+    pick_digit(hist + (int64_t(2) * heads + hd.bh) * kBuckets, uint32_t(hd.Kc), d, above, tmp,
+               sel);
+    // Kc = 0 keeps no candidate: a threshold above every key (keys are at
+    // most 0x7f800000), with nothing above or equal to it in any chunk.
+    const bool none = hd.Kc == 0;
+    const uint32_t T = none ? 0xffffffffu : (prefix << kWidth[2]) | d;
+    if (none) above = 0;
     const uint32_t need = uint32_t(hd.Kc) - above;   // T-valued tokens to keep, lowest first
-    // tokens above / equal to T in the chunks before this one
-    uint64_t before = 0;
-    for (int c = t; c < int(blockIdx.x); c += kThreads)
-      before += (uint64_t(cnt[(int64_t(hd.bh) * nch + c) * 2]) << 32) |
-                cnt[(int64_t(hd.bh) * nch + c) * 2 + 1];
-    uint64_t carry;
-    block_excl_scan_u64(before, tmp, &carry);
-    uint32_t carry_gt = uint32_t(carry >> 32), carry_eq = uint32_t(carry & 0xffffffffu);
+    // Tokens above / equal to T in the chunks before this one, from the
+    // tables of the last histogram pass (d < 1024 whenever Kc > 0), summed
+    // by the first wave.
+    if (t < 64) {
+      uint64_t before = 0;
+      if (!none) {
+        for (int c = t; c < int(blockIdx.x); c += 64) {
+          const uint32_t* tb = tab + (int64_t(hd.bh) * nch + c) * kSelectTabStride;
+          const int dc = min(int(d), kLastBins);    // reads stay inside the chunk's table
+          const uint32_t s_d = tb[dc], s_d1 = tb[min(dc + 1, kLastBins)];
+          before += (uint64_t(tb[kLastBins + 1] + s_d1) << 32) | (s_d - s_d1);
+        }
+      }
+      before = wave_incl_scan_u64(before);
+      if (t == 63) tmp[16] = before;
+    }
+    __syncthreads();
+    uint32_t carry_gt = uint32_t(tmp[16] >> 32), carry_eq = uint32_t(tmp[16] & 0xffffffffu);
+    __syncthreads();                               // tmp is reused by the scans below
     const bool vrank = hd.vec && (reinterpret_cast<uintptr_t>(rank) % 16) == 0;
     for (int base = hd.j0; base < hd.j1; base += kStep) {
       const int j0 = base + kPer * t;
@@ -331,27 +348,27 @@ SelectPlan select_plan(const Shape& sh) {
 }
 
 hipError_t launch_select(const Shape& sh, const float* scores, const int32_t* budget,
-                         int32_t* idx, int32_t* rank, char* ws, hipStream_t st) {
+                         int32_t* idx, int32_t* rank, char* ws, hipStream_t st, bool cleared) {
   const StepWs lay = step_ws_layout(sh);
   const SelectPlan p = select_plan(sh);
   const int heads = sh.B * sh.Hq;
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + lay.sel_hist);
   uint32_t* state = reinterpret_cast<uint32_t*>(ws + lay.sel_state);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + lay.sel_cnt);
-  const int64_t nh = int64_t(heads) * kBuckets;   // level 0; level 0's pass clears the others
-  sel_clear<<<unsigned((nh + 255) / 256), 256, 0, st>>>(hist, nh);
+  uint32_t* tab = reinterpret_cast<uint32_t*>(ws + lay.sel_tab);
+  if (!cleared) {
+    const int64_t nh = int64_t(heads) * kBuckets;   // level 0; level 0's pass clears the others
+    sel_clear<<<unsigned((nh + 255) / 256), 256, 0, st>>>(hist, nh);
+  }
   const dim3 grid(p.nch, heads);
   const int bb = sh.bud_b(), bhh = sh.bud_h(), keep = sh.keep();
-  sel_level<0><<<grid, kThreads, 0, st>>>(scores, budget, hist, state, heads, sh.Hq, sh.L, bb, bhh,
-                                          keep, p.chunk);
-  sel_level<1><<<grid, kThreads, 0, st>>>(scores, budget, hist, state, heads, sh.Hq, sh.L, bb, bhh,
-                                          keep, p.chunk);
-  sel_level<2><<<grid, kThreads, 0, st>>>(scores, budget, hist, state, heads, sh.Hq, sh.L, bb, bhh,
-                                          keep, p.chunk);
-  sel_count<<<grid, kThreads, 0, st>>>(scores, budget, hist, state, cnt, heads, sh.Hq, sh.L, bb,
-                                       bhh, keep, p.chunk, p.nch);
-  sel_compact<<<dim3(p.ngrid, heads), kThreads, 0, st>>>(scores, budget, state, cnt, idx, rank,
-                                                         heads, sh.Hq, sh.L, bb, bhh, keep,
+  sel_level<0><<<grid, kThreads, 0, st>>>(scores, budget, hist, state, tab, heads, sh.Hq, sh.L,
+                                          bb, bhh, keep, p.chunk, p.nch);
+  sel_level<1><<<grid, kThreads, 0, st>>>(scores, budget, hist, state, tab, heads, sh.Hq, sh.L,
+                                          bb, bhh, keep, p.chunk, p.nch);
+  sel_level<2><<<grid, kThreads, 0, st>>>(scores, budget, hist, state, tab, heads, sh.Hq, sh.L,
+                                          bb, bhh, keep, p.chunk, p.nch);
+  sel_compact<<<dim3(p.ngrid, heads), kThreads, 0, st>>>(scores, budget, hist, state, tab, idx,
+                                                         rank, heads, sh.Hq, sh.L, bb, bhh, keep,
                                                          p.chunk, p.nch);
   return hipGetLastError();
 }

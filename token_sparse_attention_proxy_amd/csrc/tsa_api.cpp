@@ -139,6 +139,10 @@ tsa_status stream_device(hipStream_t st, int* dev) {
   return TSA_OK;
 }
 
+tsa_status run_forward_fused(const tsa::Shape& sh, const void* q, const void* k, const void* v,
+                             void* o, int32_t* budget, int32_t* idx, char* base, hipStream_t st,
+                             const char* what);
+
 #define TSA_TRY(expr)                 \
   do {                                \
     tsa_status st_ = (expr);          \
@@ -166,18 +170,26 @@ StepWs step_ws_layout(const Shape& s) {
   w.bud_hmass = off;
   off = align256(off + sizeof(uint64_t) * rows * kBudgetLogBuckets);
   w.bud_ncand = off;
-  off = align256(off + sizeof(uint32_t) * rows);
-  w.bud_state = off;
-  off = align256(off + sizeof(uint64_t) * 4 * rows);
+  off = align256(off + sizeof(uint32_t) * 2 * rows);
   const size_t heads = size_t(s.B) * s.Hq;
   w.sel_hist = off;
   off = align256(off + sizeof(uint32_t) * 3 * heads * kSelectBuckets);
   w.sel_state = off;
   off = align256(off + sizeof(uint32_t) * 3 * heads * 2);
-  w.sel_cnt = off;
-  off = align256(off + sizeof(uint32_t) * heads * size_t(select_plan(s).nch) * 2);
+  w.sel_tab = off;
+  off = align256(off + sizeof(uint32_t) * heads * size_t(select_plan(s).nch) * kSelectTabStride);
   w.total = off;
   return w;
+}
+
+StepClear step_clear(const Shape& s, char* ws) {
+  const StepWs w = step_ws_layout(s);
+  StepClear c;
+  c.p0 = reinterpret_cast<uint32_t*>(ws + w.bud_hcnt);
+  c.n0 = budget_clear_words(s);
+  c.p1 = reinterpret_cast<uint32_t*>(ws + w.sel_hist);   // the first level's histograms
+  c.n1 = int64_t(s.B) * s.Hq * kSelectBuckets;
+  return c;
 }
 
 FwdWs fwd_ws_layout(const Shape& s) {
@@ -382,16 +394,23 @@ tsa_status tsa_forward(const tsa_problem* prob, const void* q, const void* k, co
   if (fault_injected()) return injected("tsa_forward");
   char* base = static_cast<char*>(ws);
   hipStream_t st = hipStream_t(stream);
+  // Up to 32K tokens the attention reading K and V through the index set
+  // (the fused path) is faster than writing the compact copies and reading
+  // them back; the bits are the same.
+  if (sh.L <= tsa::kForwardFusedMaxL)
+    return run_forward_fused(sh, q, k, v, o, budget, idx, base, st, "tsa_forward");
   float* scores = reinterpret_cast<float*>(base + f.scores);
   int32_t* rank = reinterpret_cast<int32_t*>(base + f.rank);
   void* kc = base + f.kc;
   void* vc = base + f.vc;
   hipError_t err;
-  if ((err = tsa::launch_score(sh, q, k, scores, base, st)) != hipSuccess)
+  // the scoring pass zeroes what the budget and the selection start from
+  const tsa::StepClear clr = tsa::step_clear(sh, base);
+  if ((err = tsa::launch_score(sh, q, k, scores, base, st, &clr)) != hipSuccess)
     return launched(err, "tsa_forward/score");
-  if ((err = tsa::launch_budget(sh, scores, budget, base, st)) != hipSuccess)
+  if ((err = tsa::launch_budget(sh, scores, budget, base, st, true)) != hipSuccess)
     return launched(err, "tsa_forward/budget");
-  if ((err = tsa::launch_select(sh, scores, budget, idx, rank, base, st)) != hipSuccess)
+  if ((err = tsa::launch_select(sh, scores, budget, idx, rank, base, st, true)) != hipSuccess)
     return launched(err, "tsa_forward/select");
   // Compression of K and V (each source row read once, written to every head
   // that selected it); the attention reads Q and writes O through the index
@@ -463,11 +482,12 @@ tsa_status run_forward_fused(const tsa::Shape& sh, const void* q, const void* k,
   float* scores = reinterpret_cast<float*>(base + f.scores);
   int32_t* rank = reinterpret_cast<int32_t*>(base + f.rank);
   hipError_t err;
-  if ((err = tsa::launch_score(sh, q, k, scores, base, st)) != hipSuccess)
+  const tsa::StepClear clr = tsa::step_clear(sh, base);
+  if ((err = tsa::launch_score(sh, q, k, scores, base, st, &clr)) != hipSuccess)
     return launched(err, what);
-  if ((err = tsa::launch_budget(sh, scores, budget, base, st)) != hipSuccess)
+  if ((err = tsa::launch_budget(sh, scores, budget, base, st, true)) != hipSuccess)
     return launched(err, what);
-  if ((err = tsa::launch_select(sh, scores, budget, idx, rank, base, st)) != hipSuccess)
+  if ((err = tsa::launch_select(sh, scores, budget, idx, rank, base, st, true)) != hipSuccess)
     return launched(err, what);
   if ((err = tsa::launch_zero_unselected(sh, rank, o, st)) != hipSuccess)
     return launched(err, what);

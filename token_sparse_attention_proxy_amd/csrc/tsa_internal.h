@@ -16,6 +16,7 @@ constexpr int kMaxScoreTiles = 92;    // 32-row proxy tiles per query head (bf16
 constexpr int kMaxHq = 4096;           // keeps the budget's integer masses below 2^63
 constexpr int64_t kMaxL = int64_t(1) << 22;   // per-head tensors stay below 2^31 bytes
 constexpr int kMaxHeads = 65535;       // B*Hq: grid y of the per-head launches
+constexpr int kForwardFusedMaxL = 32768;   // tsa_forward takes the fused kernels up to this L
 
 // ---------------------------------------------------------------- shapes
 struct Shape {
@@ -38,6 +39,7 @@ struct Shape {
 
 constexpr int kBudgetLogBuckets = 4096;   // log-scale buckets of the budget's first pass
 constexpr int kSelectBuckets = 2048;      // digit buckets of the selection's histogram passes
+constexpr int kSelectTabStride = 1026;    // words per chunk table of the selection's last pass
 
 // Chunking of the selection: each head's candidates in `nch` chunks of
 // `chunk` tokens (one workgroup each); the compaction grid covers L in
@@ -56,11 +58,12 @@ struct StepWs {
   size_t bud_cand;    // uint64 [R*L]: values of each row's crossing bucket
   size_t bud_hcnt;    // uint32 [R*4096]: log-bucket counts   } cleared together:
   size_t bud_hmass;   // uint64 [R*4096]: log-bucket masses   } contiguous, in
-  size_t bud_ncand;   // uint32 [R]: candidates per row       } this order
-  size_t bud_state;   // uint64 [R*4]: crossing bucket, mass and count below it, crossed
+  size_t bud_ncand;   // uint32 [2R]: candidates, finished    } this order
+                      //   extract workgroups per row        }
   size_t sel_hist;    // uint32 [3*B*Hq*2048]: selection histograms, one per digit level
   size_t sel_state;   // uint32 [3*B*Hq*2]: (prefix, count above) after each level's pick
-  size_t sel_cnt;     // uint32 [B*Hq*nch*2]: tokens above / equal to the threshold per chunk
+  size_t sel_tab;     // uint32 [B*Hq*nch*1026]: per chunk, suffix sums of the last digit and
+                      //   the count above the 22-bit prefix
   size_t total;
 };
 StepWs step_ws_layout(const Shape& s);
@@ -76,14 +79,29 @@ struct FwdWs {
 };
 FwdWs fwd_ws_layout(const Shape& s);
 
+// Words the budget and the selection need zeroed before they start: the
+// whole op has its scoring pass clear them (score_merge), so those steps
+// launch no clear kernels of their own.
+struct StepClear {
+  uint32_t* p0;
+  int64_t n0;
+  uint32_t* p1;
+  int64_t n1;
+};
+int64_t budget_clear_words(const Shape& s);   // from bud_hcnt on
+StepClear step_clear(const Shape& s, char* ws);
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipGetLastError() after enqueueing its kernels on `st`.
 hipError_t launch_score(const Shape& s, const void* q, const void* k, float* scores,
-                        char* ws, hipStream_t st);
+                        char* ws, hipStream_t st, const StepClear* clear = nullptr);
+// cleared = true: the histograms and counters the step starts from are
+// already zero (the whole op clears them in its scoring pass, clear_steps).
 hipError_t launch_budget(const Shape& s, const float* scores, int32_t* budget, char* ws,
-                         hipStream_t st);
+                         hipStream_t st, bool cleared = false);
 hipError_t launch_select(const Shape& s, const float* scores, const int32_t* budget,
-                         int32_t* idx, int32_t* rank, char* ws, hipStream_t st);
+                         int32_t* idx, int32_t* rank, char* ws, hipStream_t st,
+                         bool cleared = false);
 // qc == nullptr: K and V only.
 hipError_t launch_gather(const Shape& s, const void* q, const void* k, const void* v,
                          const int32_t* idx, const int32_t* budget, void* qc, void* kc,
