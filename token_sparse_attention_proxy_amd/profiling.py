@@ -12,9 +12,9 @@ Three sub-commands, meant to run under rocprofv3 and after it:
           indexed attention's reads follow the real index sets);
         forward: tsa_forward on the workload's own seeded inputs (its
           attention reads Q and writes O through the real index sets);
-        all: tsa_forward, then the gather of Q, K and V and the scatter
-          entry points on the same index sets, so that every kernel of the
-          library's 128K op runs once on real data.
+        all: tsa_forward, then the score, budget, select, gather (Q, K and
+          V) and scatter entry points on the same inputs and index sets, so
+          that every kernel of the library's 128K op runs on real data.
       Run it twice under ``rocprofv3 --pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``.
 
   python -m token_sparse_attention_proxy_amd.profiling summarize \\
@@ -61,9 +61,8 @@ def step_kernels(d: int, vpr: int) -> dict:
     vectors per row."""
     return {
         "score": [f"score_mfma_rowstats<{d}>", "score_merge", f"score_mfma_colsum<{d}>"],
-        "budget": ["clear_words", "budget_sigma", "budget_extract", "budget_cut"],
-        "select": ["sel_clear", "sel_level<0>", "sel_level<1>", "sel_level<2>", "sel_count",
-                   "sel_compact"],
+        "budget": ["clear_words", "budget_sigma", "budget_extract_cut"],
+        "select": ["sel_clear", "sel_level<0>", "sel_level<1>", "sel_level<2>", "sel_compact"],
         "gather": [f"gather_rows<{vpr}, true, 32>"],
         "gather_kv": [f"gather_kv_by_rank<{vpr}>"],
         "scatter": [f"scatter_rows<{vpr}>"],
@@ -122,13 +121,15 @@ def cmd_run(args):
     if args.path == "all":
         o, bud, idx = T.tsa_forward(prob, qd, kd, vd)
         s = torch.empty((wl.B, wl.Hq, wl.L), dtype=torch.float32, device=dev)
-        _, rank = T.tsa_select(prob, T.tsa_score(prob, qd, kd, s), bud)
+        T.tsa_score(prob, qd, kd, s)
+        T.tsa_budget(prob, s)            # the entry point alone, with its own clear launch
+        _, rank = T.tsa_select(prob, s, bud)
         qc, kc, vc = T.tsa_gather(prob, qd, kd, vd, idx, bud)
         del qc, kc, vc
         oc = torch.zeros_like(o)
         T.tsa_scatter(prob, oc, rank, o)
         torch.cuda.synchronize()
-        print(f"ran copy of {COPY_BYTES} B, tsa_forward, score, select, gather and scatter on "
+        print(f"ran copy of {COPY_BYTES} B, tsa_forward, score, budget, select, gather and scatter on "
               f"{wl.name}, budget {bud.cpu().tolist()}")
         return
     if args.path in ("fused", "forward"):
@@ -328,8 +329,8 @@ def cmd_traffic_summary(args):
            args.command, "```", "",
            "`profiling.py run --path all` copies 1 GiB device to device (the runtime blit "
            "`__amd_rocclr_copyBuffer`, the calibration), then runs `tsa_forward`, `tsa_score`, "
-           "`tsa_select`, `tsa_gather` (Q, K and V) and `tsa_scatter` on the workload's own "
-           "seeded inputs. The blit reads FETCH_SIZE = 0.5 GiB and WRITE_SIZE = 1 GiB for 1 GiB "
+           "`tsa_budget`, `tsa_select`, `tsa_gather` (Q, K and V) and `tsa_scatter` on the "
+           "workload's own seeded inputs. The blit reads FETCH_SIZE = 0.5 GiB and WRITE_SIZE = 1 GiB for 1 GiB "
            "moved each way, so FETCH_SIZE is scaled by 2 and WRITE_SIZE by 1 "
            "(`profiles/traffic.json` holds the exact factors and each kernel source's hash; "
            "`bench.py` reports these bytes only while the hash matches). Times are the per-kernel "
