@@ -276,7 +276,7 @@ tsa_status tsa_forward_fused(const tsa_problem* prob, const void* q, const void*
  * and output.
  *   - TSA_ERR_UNSUPPORTED when the problem's scratch
  *     (tsa_fused_workspace_bytes) exceeds TSA_NOALLOC_SCRATCH_BYTES;
- *     about 49 MiB at B=1, Hq=32, L=128K, w=64.
+ *     about 55 MiB at B=1, Hq=32, L=128K, w=64.
  *   - The scratch is resolved on the stream's device (the current device for
  *     the null stream) on its first call there; make that first call outside
  *     graph capture.
