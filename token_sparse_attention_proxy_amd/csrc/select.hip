@@ -229,16 +229,39 @@ __global__ __launch_bounds__(kThreads) void sel_level(const float* __restrict__ 
   }
 }
 
+// Zeroes row j0 + 4 * l + q of o (vpr 16-byte vectors per row) for every
+// lane l whose bit is set in the wave-uniform mask m: 64 / vpr rows per store
+// instruction, lanes split as (row of the instruction, vector of the row).
+__device__ __forceinline__ void zero_masked_rows(u32x4* __restrict__ o, int64_t hrow, int j0, int q,
+                                                 uint64_t m, int vpr) {
+  const int lane = threadIdx.x & 63;
+  const int per = 64 / vpr, sub = lane / vpr, vec = lane % vpr;
+  while (m) {
+    int row = -1;                                  // this lane's token among the next `per`
+    for (int i = 0; i < per; ++i) {
+      const int bit = m ? __builtin_ctzll(m) : -1;
+      m &= m - 1;
+      if (i == sub) row = bit;
+    }
+    if (row >= 0)
+      __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u},
+                                  o + (hrow + j0 + 4 * row + q) * vpr + vec);
+  }
+}
+
 // Picks the last digit (so T is known), then the ascending compaction of
 // each chunk, then the kept window and the -1 fill, split over the
-// workgroups by position.  Grid x covers ceil(L / chunk).
+// workgroups by position.  Grid x covers ceil(L / chunk).  With zo set (the
+// whole op), the rows of zo [B,Hq,L,vpr*16 bytes] of the candidates left out
+// are zeroed as they are found, the decompression's zero part.
 __global__ __launch_bounds__(kThreads) void sel_compact(const float* __restrict__ s,
                                                         const int32_t* __restrict__ budget,
                                                         const uint32_t* __restrict__ hist,
                                                         const uint32_t* __restrict__ state,
                                                         const uint32_t* __restrict__ tab,
                                                         int32_t* __restrict__ idx,
-                                                        int32_t* __restrict__ rank, int heads,
+                                                        int32_t* __restrict__ rank,
+                                                        u32x4* __restrict__ zo, int vpr, int heads,
                                                         int Hq, int L, int bud_b, int bud_h,
                                                         int keep, int chunk, int nch) {
   __shared__ uint64_t tmp[17];
@@ -314,6 +337,13 @@ __global__ __launch_bounds__(kThreads) void sel_compact(const float* __restrict_
         for (int q = 0; q < kPer; ++q)
           if (j0 + q < hd.j1) rh[j0 + q] = rk[q];
       }
+      if (zo) {                                    // uniform over the grid
+        const int jw = base + kPer * 64 * (t >> 6);   // first token of this wave's step
+#pragma unroll
+        for (int q = 0; q < kPer; ++q)
+          zero_masked_rows(zo, int64_t(hd.bh) * L, jw, q,
+                           __ballot(j0 + q < hd.j1 && rk[q] < 0), vpr);
+      }
 #pragma unroll
       for (int q = 0; q < kPer; ++q) u[q] = un[q];
       carry_gt += uint32_t(tot >> 32);
@@ -348,7 +378,8 @@ SelectPlan select_plan(const Shape& sh) {
 }
 
 hipError_t launch_select(const Shape& sh, const float* scores, const int32_t* budget,
-                         int32_t* idx, int32_t* rank, char* ws, hipStream_t st, bool cleared) {
+                         int32_t* idx, int32_t* rank, char* ws, hipStream_t st, bool cleared,
+                         void* zero_o) {
   const StepWs lay = step_ws_layout(sh);
   const SelectPlan p = select_plan(sh);
   const int heads = sh.B * sh.Hq;
@@ -367,9 +398,9 @@ hipError_t launch_select(const Shape& sh, const float* scores, const int32_t* bu
                                           bb, bhh, keep, p.chunk, p.nch);
   sel_level<2><<<grid, kThreads, 0, st>>>(scores, budget, hist, state, tab, heads, sh.Hq, sh.L,
                                           bb, bhh, keep, p.chunk, p.nch);
-  sel_compact<<<dim3(p.ngrid, heads), kThreads, 0, st>>>(scores, budget, hist, state, tab, idx,
-                                                         rank, heads, sh.Hq, sh.L, bb, bhh, keep,
-                                                         p.chunk, p.nch);
+  sel_compact<<<dim3(p.ngrid, heads), kThreads, 0, st>>>(
+      scores, budget, hist, state, tab, idx, rank, static_cast<u32x4*>(zero_o),
+      int(sh.row_bytes() / 16), heads, sh.Hq, sh.L, bb, bhh, keep, p.chunk, p.nch);
   return hipGetLastError();
 }
 

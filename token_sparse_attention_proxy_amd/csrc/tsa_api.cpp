@@ -410,16 +410,15 @@ tsa_status tsa_forward(const tsa_problem* prob, const void* q, const void* k, co
     return launched(err, "tsa_forward/score");
   if ((err = tsa::launch_budget(sh, scores, budget, base, st, true)) != hipSuccess)
     return launched(err, "tsa_forward/budget");
-  if ((err = tsa::launch_select(sh, scores, budget, idx, rank, base, st, true)) != hipSuccess)
+  // the selection's compaction also zeroes the rows of o it leaves out
+  if ((err = tsa::launch_select(sh, scores, budget, idx, rank, base, st, true, o)) != hipSuccess)
     return launched(err, "tsa_forward/select");
   // Compression of K and V (each source row read once, written to every head
   // that selected it); the attention reads Q and writes O through the index
-  // set, and the unselected rows are zeroed: the same bits as gather,
-  // attention on the compact Q, K, V and scatter.
+  // set: with the zeroed rows, the same bits as gather, attention on the
+  // compact Q, K, V and scatter.
   if ((err = tsa::launch_gather_kv_by_rank(sh, k, v, rank, kc, vc, st)) != hipSuccess)
     return launched(err, "tsa_forward/gather");
-  if ((err = tsa::launch_zero_unselected(sh, rank, o, st)) != hipSuccess)
-    return launched(err, "tsa_forward/zero");
   if ((err = tsa::launch_attention_qo(sh, q, kc, vc, budget, idx, o, st)) != hipSuccess)
     return launched(err, "tsa_forward/attention");
   return ok();
@@ -487,9 +486,8 @@ tsa_status run_forward_fused(const tsa::Shape& sh, const void* q, const void* k,
     return launched(err, what);
   if ((err = tsa::launch_budget(sh, scores, budget, base, st, true)) != hipSuccess)
     return launched(err, what);
-  if ((err = tsa::launch_select(sh, scores, budget, idx, rank, base, st, true)) != hipSuccess)
-    return launched(err, what);
-  if ((err = tsa::launch_zero_unselected(sh, rank, o, st)) != hipSuccess)
+  // the selection's compaction also zeroes the rows of o it leaves out
+  if ((err = tsa::launch_select(sh, scores, budget, idx, rank, base, st, true, o)) != hipSuccess)
     return launched(err, what);
   if ((err = tsa::launch_attention(sh, q, k, v, budget, idx, sh.Hq / sh.Hkv, o, st)) != hipSuccess)
     return launched(err, what);

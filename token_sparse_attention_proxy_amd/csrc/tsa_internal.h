@@ -99,9 +99,12 @@ hipError_t launch_score(const Shape& s, const void* q, const void* k, float* sco
 // already zero (the whole op clears them in its scoring pass, clear_steps).
 hipError_t launch_budget(const Shape& s, const float* scores, int32_t* budget, char* ws,
                          hipStream_t st, bool cleared = false);
+// zero_o != nullptr: the compaction also zeroes the rows of zero_o ([B,Hq,L,d])
+// of the candidates it leaves out (launch_zero_unselected's work, when no
+// kept window is in force: the window's rows are always selected).
 hipError_t launch_select(const Shape& s, const float* scores, const int32_t* budget,
                          int32_t* idx, int32_t* rank, char* ws, hipStream_t st,
-                         bool cleared = false);
+                         bool cleared = false, void* zero_o = nullptr);
 // qc == nullptr: K and V only.
 hipError_t launch_gather(const Shape& s, const void* q, const void* k, const void* v,
                          const int32_t* idx, const int32_t* budget, void* qc, void* kc,
