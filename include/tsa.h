@@ -211,7 +211,9 @@ tsa_status tsa_scatter(const tsa_problem* prob, const void* oc, const int32_t* r
 /* The whole op: score -> budget -> select -> gather -> attention -> scatter,
  * run as tsa_score -> tsa_budget -> tsa_select -> tsa_gather of K and V ->
  * tsa_zero_unselected -> tsa_attention_qo_indexed, which gives the same bits
- * without materialising the compact Q and O.  For L <= 32768 it runs the
+ * without materialising the compact Q and O (the zeroing of the unselected
+ * rows is done by the selection's last pass, as it finds them, rather than
+ * by a launch of its own).  For L <= 32768 it runs the
  * kernels of tsa_forward_fused instead (the attention reads K and V through
  * the index set, faster at those lengths), with the same bits again.
  * o: [B,Hq,L,d] output (unselected rows exactly zero); budget: [B] int32
@@ -255,7 +257,8 @@ tsa_status tsa_attention_qo_indexed(const tsa_problem* prob, const void* q, cons
 tsa_status tsa_zero_unselected(const tsa_problem* prob, const int32_t* rank, void* o, void* stream);
 
 /* The whole op with the fused kernel: score -> budget -> select ->
- * tsa_zero_unselected -> tsa_attention_indexed.  Same arguments and the
+ * tsa_zero_unselected -> tsa_attention_indexed (the zeroing again done by
+ * the selection's last pass).  Same arguments and the
  * same results, bit for bit, as tsa_forward, without the compact K and V
  * (the attention reads them through the index set): ws must hold
  * tsa_fused_workspace_bytes(prob) bytes. */
