@@ -134,9 +134,14 @@ def cmd_run(args):
         return
     if args.path in ("fused", "forward"):
         run = T.tsa_forward_fused if args.path == "fused" else T.tsa_forward
-        o, bud, _ = run(prob, qd, kd, vd)
+        o, bud, idx = run(prob, qd, kd, vd)
+        nbytes = (T.fused_workspace_bytes(prob) if args.path == "fused"
+                  else T.forward_workspace_bytes(prob))
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        for _ in range(args.reps - 1):      # back to back on the same buffers
+            run(prob, qd, kd, vd, o, bud, idx, ws)
         torch.cuda.synchronize()
-        print(f"ran copy of {COPY_BYTES} B and {run.__name__} on {wl.name}, "
+        print(f"ran copy of {COPY_BYTES} B and {run.__name__} x{args.reps} on {wl.name}, "
               f"budget {bud.cpu().tolist()}")
         return
     g = torch.Generator(device=dev).manual_seed(0)
@@ -311,6 +316,68 @@ def cmd_trace_summary(args):
     for n, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
         out.append(f"| `{n}` | {len(v)} | {sum(v) / len(v):.4f} | {min(v):.4f} | {max(v):.4f} | "
                    f"{100 * sum(v) / total:.2f}% |")
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def cmd_op_trace(args):
+    """Kernel trace of `run --path forward|fused --reps N`: the op's own kernels in launch
+    order, each op instance starting at its first scoring pass; the first instance is left
+    out (cold), the others averaged position by position."""
+    wl, hdr = _shape_header(args.workload)
+    rows = sorted(csv.DictReader(open(_first(args.trace, "*kernel_trace.csv"))),
+                  key=lambda r: int(r["Start_Timestamp"]))
+    rows = [r for r in rows if kernel_source(short_name(r["Kernel_Name"])) is not None]
+    first = short_name(rows[0]["Kernel_Name"])
+    ops, cur = [], []
+    for r in rows:
+        if short_name(r["Kernel_Name"]) == first and cur:
+            ops.append(cur)
+            cur = []
+        cur.append(r)
+    ops.append(cur)
+    if len(ops) < 2:
+        raise SystemExit("need at least two op instances (run --reps 2 or more)")
+    warm = ops[1:]
+    names = [short_name(r["Kernel_Name"]) for r in warm[0]]
+    if any([short_name(r["Kernel_Name"]) for r in op] != names for op in warm):
+        raise SystemExit("op instances differ in their kernel sequence")
+    dur = [[(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in op] for op in warm]
+    span = [(int(op[-1]["End_Timestamp"]) - int(op[0]["Start_Timestamp"])) / 1e3 for op in warm]
+    steps = {}
+    for st, ks in step_kernels(wl.d, wl.d * (2 if wl.dtype == "bf16" else 4) // 16).items():
+        for k in ks:
+            steps.setdefault(k, st)
+    out = [f"# Kernel trace of the op: {wl.L // 1024}K workload ({hdr})", "",
+           "Command (from the repository root `$R`, on one MI355X):", "", "```",
+           args.command, "```", "",
+           f"`profiling.py run --path {args.path} --reps {len(ops)}` runs the op {len(ops)} "
+           "times back to back on the same buffers (after the 1 GiB calibration copy). Each "
+           "row is one kernel launch of the op, in launch order, averaged over the instances "
+           f"after the first ({len(warm)}): its duration from the trace's start and end "
+           "timestamps.", "",
+           "| # | kernel | step | mean µs | min µs | max µs |", "|---|---|---|---|---|---|"]
+    tot_other = 0.0
+    per_step = {}
+    for i, n in enumerate(names):
+        v = [d[i] for d in dur]
+        m = sum(v) / len(v)
+        step = "attention" if n.startswith("attn_fwd") else steps.get(n, "")
+        if n == "score_merge":
+            step = "score (+ clears)"
+        if n == "sel_compact":
+            step = "select (+ zero fill)"
+        if not n.startswith("attn_fwd"):
+            tot_other += m
+        per_step[step.split(" ")[0]] = per_step.get(step.split(" ")[0], 0.0) + m
+        out.append(f"| {i + 1} | `{n}` | {step} | {m:.2f} | {min(v):.2f} | {max(v):.2f} |")
+    mean_span = sum(span) / len(span)
+    attn = per_step.get("attention", 0.0)
+    out += ["", "Per step (µs): " + ", ".join(f"{k} {v:.1f}" for k, v in per_step.items()) + ".",
+            f"All kernels but the attention: {tot_other:.1f} µs, {100 * tot_other / attn:.2f}% "
+            f"of the attention's {attn:.1f} µs. From the first launch's start to the last one's "
+            f"end: {mean_span:.1f} µs on average, so the launches follow one another with "
+            f"{max(0.0, mean_span - tot_other - attn):.1f} µs between them in all."]
     open(args.out, "w").write("\n".join(out) + "\n")
     print("\n".join(out))
 
@@ -513,7 +580,15 @@ def main():
     r.add_argument("--workload", default="llama8b_bf16_L128k")
     r.add_argument("--budget", type=int, default=123997)
     r.add_argument("--path", choices=sorted(KERNEL_ARGS) + ["all"], default="fused")
+    r.add_argument("--reps", type=int, default=1, help="op runs (paths fused and forward)")
     r.set_defaults(fn=cmd_run)
+    ot = sub.add_parser("op-trace")
+    ot.add_argument("--trace", required=True, help="rocprofv3 --kernel-trace output dir")
+    ot.add_argument("--workload", default="llama8b_bf16_L128k")
+    ot.add_argument("--path", choices=["forward", "fused"], default="forward")
+    ot.add_argument("--command", required=True)
+    ot.add_argument("--out", required=True)
+    ot.set_defaults(fn=cmd_op_trace)
     s = sub.add_parser("summarize")
     s.add_argument("--fetch", required=True)
     s.add_argument("--write", required=True)
