@@ -19,8 +19,25 @@ from token_sparse_attention_proxy_amd import build as tsa_build
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
+def _kernel_objects_current() -> bool:
+    """The normal build's objects exist and are newer than their sources and headers."""
+    heads = [os.path.join(tsa_build.CSRC, h) for h in os.listdir(tsa_build.CSRC) if h.endswith(".h")]
+    heads += [os.path.join(tsa_build.INCLUDE, h) for h in os.listdir(tsa_build.INCLUDE)]
+    newest_head = max(os.path.getmtime(h) for h in heads)
+    for src in tsa_build.SOURCES:
+        obj = os.path.join(tsa_build.BUILD, os.path.splitext(src)[0] + ".o")
+        if not os.path.exists(obj):
+            return False
+        t = os.path.getmtime(obj)
+        if t < os.path.getmtime(os.path.join(tsa_build.CSRC, src)) or t < newest_head:
+            return False
+    return True
+
+
 def test_host_code_under_sanitizers(tmp_path):
     out = str(tmp_path)
+    if not _kernel_objects_current():
+        tsa_build.build()
     tsa_build.build_host_sanitized(out)
     exe = os.path.join(out, "abi_host_check")
     cmd = [tsa_build.CLANG, "-O1", "-g", "-std=c11", "-Wall", "-Werror",
