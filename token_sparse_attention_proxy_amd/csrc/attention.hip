@@ -309,14 +309,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
 #pragma unroll
     for (int e = 0; e < 16; ++e) bias[e] = -m;
   };
-  float l_run = 0.f;      // this lane's share of the row sum
+  // This lane's share of the row sum, as four independent partial sums kept
+  // across the whole key walk (pair p of a subtile adds into lsum[p % 4]).
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+  auto clear_sum = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lsum[i] = 0.f;
+  };
+  auto row_sum = [&]() { return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]); };
 
   // P = exp2(S - m_ref) (biased: S^T already holds -m_ref from its chain start),
   // rounded to bf16; fp32 row sums of P (four partial sums), then O^T += V^T P^T.
   auto pv = [&](int buf, const f32x16 (&sacc)[NSUB], bool biased) {
     const float mneg = biased ? 0.f : -m_ref;
     bf16x8 pb[NSUB * 2];
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};      // independent partial sums
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb)
 #pragma unroll
@@ -327,11 +333,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
           const float p0 = __builtin_amdgcn_exp2f(sacc[sb][8 * tt + 2 * e2] + mneg);
           const float p1 = __builtin_amdgcn_exp2f(sacc[sb][8 * tt + 2 * e2 + 1] + mneg);
           pk[e2] = pack_bf16x2(p0, p1);
-          ls[e2] += p0 + p1;
+          lsum[e2] += p0 + p1;
         }
         pb[2 * sb + tt] = __builtin_bit_cast(bf16x8, pk);
       }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
     for (int kk = 0; kk < NSUB * 2; ++kk)
 #pragma unroll
@@ -366,12 +371,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     };
     f32x16 sacc[NSUB];
     u32x4 pk[2 * NSUB];
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
     auto softmax_pair = [&](int sb, int p) {  // elements 2p, 2p+1 of subtile sb
       const float p0 = __builtin_amdgcn_exp2f(sacc[sb][2 * p]);
       const float p1 = __builtin_amdgcn_exp2f(sacc[sb][2 * p + 1]);
       pk[2 * sb + p / 4][p % 4] = pack_bf16x2(p0, p1);
-      ls[p % 4] += p0 + p1;
+      lsum[p % 4] += p0 + p1;
     };
     bf16x8 ring[PF + 1];
 #pragma unroll
@@ -397,7 +401,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
         }
       }
     }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     // Pin the operand reads PF MFMAs ahead, whatever the surrounding code,
     // and spread the tile's 32 exps evenly from a quarter chain after the
     // first S^T chain ends (its accumulator is then ready), so the row-sum
@@ -545,7 +548,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
       }
 #pragma unroll
       for (int i = 0; i < DT; ++i) oacc[i] = zero;
-      l_run = 0.f;
+      clear_sum();
       bool have_ref = attempt == 1;      // the first tile a wave uses sets its reference
       auto bs_compute = [&](int tile, bool use, int buf) {
         if (!use) return;
@@ -605,7 +608,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
         u3 = u5;
         sb0 = (sb0 + 2) & 3;
       }
-      const bool bad = !(sum_halves(l_run) <= kSumLimit);
+      const bool bad = !(sum_halves(row_sum()) <= kSumLimit);
       if (!__syncthreads_or(bad)) break;
       continue;
     }
@@ -631,7 +634,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
     }
 #pragma unroll
     for (int i = 0; i < DT; ++i) oacc[i] = zero;
-    l_run = 0.f;
+    clear_sum();
     auto compute = [&](int tile, int buf) {
       if (tile < wdiag && tile > 0) {
         hot(buf);                       // no mask, no reductions
@@ -699,12 +702,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16(
       }
       __syncthreads();
     }
-    const bool bad = !(sum_halves(l_run) <= kSumLimit);
+    const bool bad = !(sum_halves(row_sum()) <= kSumLimit);
     if (!__syncthreads_or(bad)) break;
   }
 
   // epilogue: O = O^T / l; lane holds d = 32dt + 8g + 4*half + {0..3} of its row.
-  const float inv = 1.0f / sum_halves(l_run);
+  const float inv = 1.0f / sum_halves(row_sum());
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
