@@ -284,6 +284,42 @@ def measured_traffic(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
+def operand_dependence(prob, shape, budget, flops, st, reps: int = 3):
+    """The compact attention (the breakdown's `attention` call: same kernel, launch and
+    budget) on operands of the same shapes whose values barely toggle: all ones, and random
+    signs of powers of two (q = +-1/4, k, v = +-1; exponents and signs only, zero
+    mantissas).  The instruction stream is the same as on the real data; only the operand
+    values change.  Median of reps launches after one warm-up, HIP events on the stream."""
+    import torch
+    from token_sparse_attention_proxy_amd import tsa as T
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(11)
+    res = {}
+    for key in ("all_ones", "random_signs"):
+        if key == "all_ones":
+            one = torch.ones(shape, dtype=torch.bfloat16, device=dev)
+            q = k = v = one
+        else:
+            sgn = lambda: (torch.randint(0, 2, shape, device=dev, generator=g) * 2 - 1).to(torch.bfloat16)
+            q, k, v = sgn() * 0.25, sgn(), sgn()
+        o = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        T.tsa_attention(prob, q, k, v, budget, 1, o)
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            T.tsa_attention(prob, q, k, v, budget, 1, o)
+            e1.record(st)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        tf = flops / (ms * 1e-3) / 1e12
+        res[key] = {"ms": round(ms, 4), "TFLOP_s": round(tf, 1),
+                    "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del q, k, v, o
+    return res
+
+
 def mfma_ceiling(st, iters: int = 60000, reps: int = 2):
     """Sustained bf16 MFMA rate of a register-only loop (two waves per SIMD, four
     accumulator chains), with random and with constant operands; best of reps launches
@@ -500,6 +536,12 @@ def main():
     if ceiling:
         log(f"[bench] MFMA ceiling: random operands {ceiling['random_operands']} TFLOP/s, "
             f"constant operands {ceiling['constant_operands']} TFLOP/s")
+    # ---- the same compact attention on operands that barely toggle
+    opdep = None
+    if wl.dtype == "bf16":
+        opdep = operand_dependence(prob, shape, budget, attention_flops(budget.cpu().numpy(), wl.Hq, wl.d), st)
+        log("[bench] compact attention by operand data: real " + f"{steps_ms['attention']:.3f} ms, " +
+            ", ".join(f"{k} {v['ms']:.3f} ms (frac {v['frac']})" for k, v in opdep.items()))
 
     # ---- dense causal attention baseline (same kernel, GQA head map)
     dense_ms = None
@@ -634,6 +676,14 @@ def main():
     if ceiling:
         ceiling["attention_frac_of_random"] = round(achieved / ceiling["random_operands"], 4)
         roofline["mfma_ceiling"] = ceiling
+    if opdep:
+        att_ms = steps_ms["attention"]
+        opdep["real_data"] = {"ms": round(att_ms, 4),
+                              "frac": round(flops / (att_ms * 1e-3) / 1e12 / peak, 4)}
+        opdep["what"] = ("the compact attention (tsa_attention, kv_group 1, the headline budget) on "
+                         "the compressed tensors (real_data) and on operands of the same shapes "
+                         "that barely toggle; same kernel and instruction stream")
+        roofline["operand_dependence"] = opdep
 
     # HBM fractions of the byte-moving steps (algorithmic bytes)
     eb = 2 if bf16 else 4
