@@ -28,9 +28,12 @@ Printed as one JSON line, with:
     index sets of consecutive layers, and the stack's time against the same
     stack with dense attention;
   * a sweep over the other workloads (8K; 32K with Zipf-biased keys at
-    tau = 0.01, 0.05, 0.1; B=2 64K with 7 query heads per KV head): ms per
+    tau = 0.01, 0.05, 0.1; B=2 64K with 7 query heads per KV head; the
+    Zipf-biased keys at 128K, tau = 0.05, 0.1, 0.2): ms per
     layer of the op and of the dense attention, speedup, K/L, the share of
     the non-attention kernels and the attention's MFMA fraction;
+  * the compact attention on operands that barely toggle (all ones; random
+    signs of powers of two) beside its time on the compressed tensors;
   * beside every K/L, the importance mass the top 1% of tokens hold per
     head (how skewed the scores are, which bounds what tau can prune);
   * per kernel, the HBM bytes that rocprofv3 counters recorded for the same
@@ -776,7 +779,7 @@ def main():
     if not args.no_sweep:
         sweep = []
         for name, taus in [("llama8b_bf16_L8k", (0.05,)), ("llama8b_bf16_L32k_zipf", (0.01, 0.05, 0.1)),
-                           ("gqa7_bf16_B2_L64k", (0.1,))]:
+                           ("gqa7_bf16_B2_L64k", (0.1,)), ("llama8b_bf16_L128k_zipf", (0.05, 0.1, 0.2))]:
             log(f"[bench] sweep {name}: generating inputs")
             sweep += sweep_one(name, taus, dev, max(3, min(args.steps, 10)))
         out["sweep"] = sweep

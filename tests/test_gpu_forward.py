@@ -109,7 +109,7 @@ def test_compact_kv_steps_compose_to_forward():
 
 # ---------------------------------------------------------------- full sizes
 FULL = ["tiny_mha_f32_L1k", "llama8b_bf16_L8k", "llama8b_bf16_L32k_zipf", "llama8b_bf16_L128k",
-        "gqa7_bf16_B2_L64k"]
+        "gqa7_bf16_B2_L64k", "llama8b_bf16_L128k_zipf"]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -63,7 +63,9 @@ class Workload:
 
 # The five workloads: tiny MHA correctness case, Llama-3-8B-shaped layer at
 # 8K, the 32K tau sweep with Zipf-skewed heads, the 128K headline layer, and
-# the wide-GQA B=2 stress case.
+# the wide-GQA B=2 stress case; and a sixth, the 32K recipe (Zipf-skewed
+# heads) at the headline's 128K length, for the speedup at long context when
+# importance is concentrated.
 WORKLOADS = {
     "tiny_mha_f32_L1k": Workload("tiny_mha_f32_L1k", "f32", 1, 4, 4, 1024, 64, 16, (0.05,),
                                  plant="shared", plant_frac=0.05, plant_amp=3.0, seed_base=1000),
@@ -77,6 +79,9 @@ WORKLOADS = {
                                    seed_base=4000),
     "gqa7_bf16_B2_L64k": Workload("gqa7_bf16_B2_L64k", "bf16", 2, 28, 4, 65536, 128, 128, (0.1,),
                                   plant="half", plant_frac=0.01, plant_amp=5.0, seed_base=5000),
+    "llama8b_bf16_L128k_zipf": Workload("llama8b_bf16_L128k_zipf", "bf16", 1, 32, 8, 131072, 128,
+                                        64, (0.05, 0.1, 0.2), plant="none", zipf_s=1.1,
+                                        seed_base=6000),
 }
 
 HEADLINE = "llama8b_bf16_L128k"
