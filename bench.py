@@ -320,6 +320,7 @@ def operand_dependence(prob, shape, budget, flops, st, reps: int = 3):
         res[key] = {"ms": round(ms, 4), "TFLOP_s": round(tf, 1),
                     "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
         del q, k, v, o
+    res["launches"] = 2 * (1 + reps)
     return res
 
 
@@ -544,7 +545,8 @@ def main():
     if wl.dtype == "bf16":
         opdep = operand_dependence(prob, shape, budget, attention_flops(budget.cpu().numpy(), wl.Hq, wl.d), st)
         log("[bench] compact attention by operand data: real " + f"{steps_ms['attention']:.3f} ms, " +
-            ", ".join(f"{k} {v['ms']:.3f} ms (frac {v['frac']})" for k, v in opdep.items()))
+            ", ".join(f"{k} {v['ms']:.3f} ms (frac {v['frac']})" for k, v in opdep.items()
+                      if isinstance(v, dict)))
 
     # ---- dense causal attention baseline (same kernel, GQA head map)
     dense_ms = None

@@ -14,6 +14,7 @@ DENSE = ("void tsa::(anonymous namespace)::attn_fwd_bf16<128, false, false, fals
          "short const*, int)")
 SCORE = "void tsa::(anonymous namespace)::score_merge(HIP_vector_type<float, 2u> const*, long)"
 COPY = "__amd_rocclr_copyBuffer"
+PROBE = "void tsa::(anonymous namespace)::mfma_probe<true>(float*, int)"
 
 
 def _run(*args):
@@ -35,22 +36,29 @@ def test_trace_summary_keeps_headline_dispatches(tmp_path):
     gx = (131072 + 255) // 256 * 512
     rows = [["KERNEL_DISPATCH", ATT, 0, 100_000_000, gx, 32],
             ["KERNEL_DISPATCH", ATT, 200_000_000, 302_000_000, gx, 32],
-            ["KERNEL_DISPATCH", DENSE, 400_000_000, 510_000_000, gx, 32],
-            ["KERNEL_DISPATCH", SCORE, 520_000_000, 520_010_000, 64, 1],      # after: left out
+            ["KERNEL_DISPATCH", DENSE, 310_000_000, 409_000_000, gx, 32],    # breakdown
+            ["KERNEL_DISPATCH", PROBE, 410_000_000, 440_000_000, 256, 1],
+            ["KERNEL_DISPATCH", DENSE, 450_000_000, 520_000_000, gx, 32],    # toggle-free operands
+            ["KERNEL_DISPATCH", DENSE, 530_000_000, 600_000_000, gx, 32],
+            ["KERNEL_DISPATCH", DENSE, 700_000_000, 810_000_000, gx, 32],    # dense baseline
+            ["KERNEL_DISPATCH", SCORE, 820_000_000, 820_010_000, 64, 1],      # after: left out
             ["KERNEL_DISPATCH", "void at::native::fill(int)", 10, 20, 1, 1]]  # torch: left out
     _write(str(tmp_path / "trace" / "t_kernel_trace.csv"), hdr, rows)
     bench = {"value": 101.0, "budget": [123997],
              "roofline": {"avg_launch_ms": 101.0, "kernel": "attn_fwd_bf16<128, false, false, true>",
                           "achieved": 1247.1, "frac": 0.4988,
                           "mfma_ceiling": {"random_operands": 1700.0, "constant_operands": 2480.0,
-                                           "attention_frac_of_random": 0.7336}}}
+                                           "attention_frac_of_random": 0.7336},
+                          "operand_dependence": {"launches": 2}}}
     (tmp_path / "b.json").write_text("log line\n" + json.dumps(bench) + "\n")
     out = tmp_path / "t.md"
     _run("trace-summary", "--trace", str(tmp_path / "trace"), "--bench", str(tmp_path / "b.json"),
          "--command", "CMD", "--out", str(out))
     text = out.read_text()
     assert "| `attn_fwd_bf16<128, false, false, true>` | 2 | 101.0000 | 100.0000 | 102.0000 |" in text
-    assert "| `attn_fwd_bf16<128, false, false, false>` | 1 | 110.0000 |" in text
+    assert "| `attn_fwd_bf16<128, false, false, false> (breakdown, compressed tensors)` | 1 | 99.0000 |" in text
+    assert "| `attn_fwd_bf16<128, false, false, false> (operands that barely toggle)` | 2 | 70.0000 |" in text
+    assert "| `attn_fwd_bf16<128, false, false, false> (dense baseline)` | 1 | 110.0000 |" in text
     assert "score_merge" not in text and "fill" not in text
     assert "1700.0 TFLOP/s with random operands" in text
 

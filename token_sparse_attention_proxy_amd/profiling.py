@@ -286,20 +286,36 @@ def cmd_trace_summary(args):
     if not dense:
         raise SystemExit("no dense attention launch of the headline shape in the trace")
     end = max(int(r["End_Timestamp"]) for r in dense)
+    # The plain instantiation runs three times over in a bench run: in the per-kernel
+    # breakdown (on the compressed tensors, before the MFMA probe), then on operands that
+    # barely toggle (the bench line says how many launches), then as the dense baseline.
+    plain = f"attn_fwd_bf16<{wl.d}, false, false, false>"
+    probe_end = max((int(r["End_Timestamp"]) for r in rows
+                     if short_name(r["Kernel_Name"]).startswith("mfma_probe")), default=None)
+    n_opdep = int(bench["roofline"].get("operand_dependence", {}).get("launches", 0))
+    after_probe = 0
     per = {}
-    for r in rows:
+    for r in sorted(rows, key=lambda r: int(r["Start_Timestamp"])):
         n = short_name(r["Kernel_Name"])
         if int(r["Start_Timestamp"]) > end or (kernel_source(n) is None and
                                                not n.startswith("mfma_probe")):
             continue             # torch's own kernels (input copies, fills) are left out
-        per.setdefault(short_name(r["Kernel_Name"]), []).append(
+        if n == plain and probe_end is not None:
+            if int(r["Start_Timestamp"]) < probe_end:
+                n += " (breakdown, compressed tensors)"
+            else:
+                after_probe += 1
+                n += (" (operands that barely toggle)" if after_probe <= n_opdep
+                      else " (dense baseline)")
+        per.setdefault(n, []).append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
     total = sum(sum(v) for v in per.values())
     out = [f"# Kernel trace: bench.py on the {wl.L // 1024}K workload ({hdr})", "",
            "Command (from the repository root `$R`, on one MI355X):", "", "```",
            args.command, "```", "",
            "Per-kernel durations of every dispatch of the headline workload in that run (the "
-           "timed steps, the other path, the per-kernel breakdown, the MFMA ceiling probe and "
+           "timed steps, the other path, the per-kernel breakdown, the MFMA ceiling probe, the "
+           "compact attention on operands that barely toggle (all ones, then random signs) and "
            "the dense baseline; the parity check and the sweep that follow are left out, and so "
            "are torch's own kernels). `*_kernel_stats.csv` of the same run holds all "
            "dispatches.", "",
