@@ -117,7 +117,8 @@ def cmd_run(args):
     dst.copy_(src)                       # calibration: COPY_BYTES read, COPY_BYTES written
     torch.cuda.synchronize()
     del src, dst
-    prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, wl.taus[0], wl.dtype)
+    tau = wl.taus[0] if args.tau is None else args.tau
+    prob = T.Problem(wl.B, wl.Hq, wl.Hkv, wl.L, wl.d, wl.w, tau, wl.dtype)
     if args.path == "all":
         o, bud, idx = T.tsa_forward(prob, qd, kd, vd)
         s = torch.empty((wl.B, wl.Hq, wl.L), dtype=torch.float32, device=dev)
@@ -265,12 +266,12 @@ def _first(dirpath, pattern):
     return got[0]
 
 
-def _shape_header(wl_name):
+def _shape_header(wl_name, tau=None):
     sys.path.insert(0, ROOT)
     from token_sparse_attention_proxy_amd import inputs
     wl = inputs.WORKLOADS[wl_name]
     return wl, (f"{wl.name}: B={wl.B}, Hq={wl.Hq}, Hkv={wl.Hkv}, L={wl.L}, d={wl.d}, "
-                f"w={wl.w}, tau={wl.taus[0]}")
+                f"w={wl.w}, tau={wl.taus[0] if tau is None else tau}")
 
 
 def cmd_trace_summary(args):
@@ -340,7 +341,7 @@ def cmd_op_trace(args):
     """Kernel trace of `run --path forward|fused --reps N`: the op's own kernels in launch
     order, each op instance starting at its first scoring pass; the first instance is left
     out (cold), the others averaged position by position."""
-    wl, hdr = _shape_header(args.workload)
+    wl, hdr = _shape_header(args.workload, args.tau)
     rows = sorted(csv.DictReader(open(_first(args.trace, "*kernel_trace.csv"))),
                   key=lambda r: int(r["Start_Timestamp"]))
     rows = [r for r in rows if kernel_source(short_name(r["Kernel_Name"])) is not None]
@@ -597,11 +598,13 @@ def main():
     r.add_argument("--budget", type=int, default=123997)
     r.add_argument("--path", choices=sorted(KERNEL_ARGS) + ["all"], default="fused")
     r.add_argument("--reps", type=int, default=1, help="op runs (paths fused and forward)")
+    r.add_argument("--tau", type=float, default=None, help="default: the workload's first tau")
     r.set_defaults(fn=cmd_run)
     ot = sub.add_parser("op-trace")
     ot.add_argument("--trace", required=True, help="rocprofv3 --kernel-trace output dir")
     ot.add_argument("--workload", default="llama8b_bf16_L128k")
     ot.add_argument("--path", choices=["forward", "fused"], default="forward")
+    ot.add_argument("--tau", type=float, default=None, help="the tau the run used")
     ot.add_argument("--command", required=True)
     ot.add_argument("--out", required=True)
     ot.set_defaults(fn=cmd_op_trace)
